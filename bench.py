@@ -1,0 +1,228 @@
+"""Benchmark of the context-parallel state-correction hot path on one MI355X.
+
+Workload (one "step"): the 32K-token x 32-head forward correction in both state
+layouts -- batch 1, 32 heads, 8 segments of 4096 tokens, K = V = 128, one
+qla_correct_h0 call for kv and one for vk (512 segment-state corrections).
+Inputs are seeded synthetic data (H ~ N(0,1), M = 0.9 I + N(0, 0.1/K), S0 ~
+N(0,1)), already resident in HBM when timing starts.  Each call in a step reads
+its own buffers, and steps rotate over enough buffer sets (> 256 MB MALL) that
+every call streams its inputs from HBM.
+
+Prints one JSON line.  value = corrections/s of the whole job; roofline =
+the dominant kernel's achieved TFLOP/s (its average launch duration from HIP
+events recorded on the launch stream) against the fp32 matrix peak;
+cpu_baseline = the fp64 oracle on the host, one thread, on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "segment-state corrections/s + achieved HBM GB/s (% roofline), 32K tok × 32 heads"
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "linear_attention_context_amd", "csrc", "qla_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "correct_h0_kv_fwd_32k32h_traffic.md")
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--rotate", type=int, default=4, help="buffer sets cycled by the steps")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-check", action="store_true", help="skip the oracle check of the timed outputs")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (for scaling rocprof byte counters)")
+    return p.parse_args(argv)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
+    m_bytes = re.search(r"HBM bytes per launch \(scaled\):\s*`?([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on a "
+              "single MI355X: chains shard across GPUs with no exchange, see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import linear_attention_context_amd as qla
+    import qla_inputs as qi
+
+    case = qi.CASES[2]
+    B, NH, N, K, V = case.batch, case.heads, case.n_seg, case.K, case.V
+    variants = [("kv", "fwd"), ("vk", "fwd")]
+    H, M, S0 = qi.case_arrays(2)
+    host = {"kv": (H, S0), "vk": (qi.to_vk(H), qi.to_vk(S0))}
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # Buffer sets: every call of every step has its own H, M, S0 and out.
+    sets = []
+    for r in range(args.rotate):
+        calls = []
+        for layout, direction in variants:
+            Hl, Sl = host[layout]
+            calls.append(dict(layout=layout, direction=direction,
+                              H=torch.from_numpy(Hl).to(dev), M=torch.from_numpy(M).to(dev),
+                              S0=torch.from_numpy(Sl).to(dev),
+                              out=torch.full(Hl.shape, float("nan"), device=dev)))
+        sets.append(calls)
+    torch.cuda.synchronize()
+
+    def launch(c):
+        qla.qla_correct_h0(c["H"], c["M"], c["S0"], c["out"], c["layout"], c["direction"], B, NH, N, K, V,
+                           stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        for c in sets[i % args.rotate]:
+            launch(c)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, an event pair around every launch (on the launch stream).
+    nv = len(variants)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nv)]
+          for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        for v, c in enumerate(sets[i % args.rotate]):
+            ev[i][v][0].record(stream)
+            launch(c)
+            ev[i][v][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = t_begin.elapsed_time(t_end)
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+
+    per_call_us = {}
+    for v, (layout, direction) in enumerate(variants):
+        d = np.array([ev[i][v][0].elapsed_time(ev[i][v][1]) for i in range(args.steps)]) * 1e3
+        per_call_us[f"{layout}_{direction}"] = {"mean": float(d.mean()), "median": float(np.median(d)),
+                                               "min": float(d.min()), "max": float(d.max())}
+
+    corrections_per_step = nv * B * NH * N
+    value = corrections_per_step / (ms_per_step * 1e-3)
+    flop_per_launch = B * NH * N * 2.0 * K * K * V
+    bytes_per_launch = 4.0 * (B * NH * N * (2 * K * V + K * K) + B * NH * K * V)
+    dominant = max(per_call_us, key=lambda k: per_call_us[k]["mean"])
+    t_dom = per_call_us[dominant]["mean"] * 1e-6
+    achieved_tflops = flop_per_launch / t_dom / 1e12
+    hbm_gbps = bytes_per_launch / t_dom / 1e9
+    t_roof = max(flop_per_launch / (PEAK_FP32_MFMA_TFLOPS * 1e12), bytes_per_launch / (PEAK_HBM_GBPS * 1e9))
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "segment-state corrections/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded: H~N(0,1), M=0.9I+N(0,0.1/K), S0~N(0,1))",
+        "config": {"workload": "32K tokens x 32 heads: batch 1, 8 CP segments of 4096, K=V=128, forward, "
+                               "kv and vk layouts (one call each per step)",
+                   "batch": B, "heads": NH, "n_seg": N, "K": K, "V": V,
+                   "calls_per_step": [f"{l}_{d}" for l, d in variants], "buffer_sets": args.rotate},
+        "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_FP32_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_FP32_MFMA_TFLOPS,
+                     "traffic": read_traffic(), "kernel": f"correct_h0_kernel<128,{dominant}>",
+                     "flop_per_launch": flop_per_launch, "algorithmic_bytes_per_launch": bytes_per_launch,
+                     "hbm_gbps": hbm_gbps, "hbm_frac": hbm_gbps / PEAK_HBM_GBPS,
+                     "roofline_frac_of_max_bound": t_roof / t_dom},
+        "per_call_us": per_call_us,
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+
+    if not args.no_check:
+        # In-situ check: outputs written by the timed launches against the oracle.
+        import oracle
+        last = sets[(args.steps - 1) % args.rotate]
+        worst = 0.0
+        for c in last:
+            Hl, Sl = host[c["layout"]]
+            ref = oracle.correct_h0(Hl, M, Sl, c["layout"], c["direction"])
+            got = c["out"].cpu().numpy().astype(np.float64)
+            num = np.sqrt(((got - ref) ** 2).sum(axis=(-1, -2)))
+            den = np.sqrt((ref ** 2).sum(axis=(-1, -2)))
+            worst = max(worst, float((num / den).max()))
+        result["timed_output_max_rel_l2"] = worst
+        if not worst <= 2e-5:
+            print(json.dumps(result))
+            raise SystemExit(f"timed outputs fail parity: max rel L2 {worst:.3e}")
+
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            for layout, direction in variants:
+                Hl, Sl = host[layout]
+                oracle.correct_h0(Hl, M, Sl, layout, direction)
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": reps * corrections_per_step / el, "unit": "segment-state corrections/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the full step (kv fwd + vk fwd, {corrections_per_step} corrections) repeated {reps}x "
+                      f"in {el:.1f} s, fp64 plain loops, 1 thread",
+        }
+
+    if args.copy_calibration:
+        n = 1 << 28  # 1 GiB of fp32
+        a = torch.empty(n, device=dev)
+        b = torch.empty(n, device=dev)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = {"read": 4 * n, "written": 4 * n}
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,148 @@
+"""Python binding of libqla.so, the gfx950 context-parallel state-correction library.
+
+Argument marshalling only: every step of the correction runs in the library's
+HIP kernels.  The C ABI (include/qla.h) takes device pointers, sizes and a
+hipStream_t; these wrappers accept torch tensors (or raw integer addresses),
+pass their data pointers and the current HIP stream, and raise on a non-zero
+status.  PyTorch is used for device memory and streams only.
+
+There is no fallback: if libqla.so is missing or cannot be loaded, the first
+call raises.  Build it with ``python -m linear_attention_context_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "QLA_LAYOUT_KV", "QLA_LAYOUT_VK", "QLA_DIR_FWD", "QLA_DIR_BWD", "QLA_MAX_GROUPS",
+    "QlaError", "qla_correct_h0", "qla_correct_h0_grouped", "qla_status_str",
+    "raw_correct_h0", "raw_correct_h0_grouped", "load_library", "library_path",
+]
+
+QLA_LAYOUT_KV, QLA_LAYOUT_VK = 0, 1
+QLA_DIR_FWD, QLA_DIR_BWD = 0, 1
+QLA_MAX_GROUPS = 64
+STATUS = {
+    0: "QLA_OK", -1: "QLA_ERR_NULL", -2: "QLA_ERR_ENUM", -3: "QLA_ERR_SHAPE", -4: "QLA_ERR_ALIGN",
+    -5: "QLA_ERR_ALIAS", -6: "QLA_ERR_GROUPS", -7: "QLA_ERR_LAUNCH", -8: "QLA_ERR_MEMORY",
+}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_DEFAULT_LIB = os.path.join(_PKG, "libqla.so")
+_libs: dict = {}
+
+
+class QlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class qla_head_group(ctypes.Structure):
+    _fields_ = [("head_begin", ctypes.c_int), ("head_count", ctypes.c_int),
+                ("layout", ctypes.c_int), ("direction", ctypes.c_int)]
+
+
+def library_path(variant: str = "") -> str:
+    return os.path.join(_PKG, f"libqla{'_' + variant if variant else ''}.so")
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load (once) and return the library; raises if it is not built."""
+    path = path or _DEFAULT_LIB
+    lib = _libs.get(path)
+    if lib is not None:
+        return lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run `python -m linear_attention_context_amd.build` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(path)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.qla_correct_h0.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp]
+    lib.qla_correct_h0.restype = ci
+    lib.qla_correct_h0_grouped.argtypes = [vp, vp, vp, vp, ctypes.POINTER(qla_head_group), ci,
+                                           ci, ci, ci, ci, ci, vp]
+    lib.qla_correct_h0_grouped.restype = ci
+    lib.qla_status_str.argtypes = [ci]
+    lib.qla_status_str.restype = ctypes.c_char_p
+    _libs[path] = lib
+    return lib
+
+
+def qla_status_str(status: int, lib: ctypes.CDLL | None = None) -> str:
+    return (lib or load_library()).qla_status_str(int(status)).decode()
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr() or None
+    raise TypeError(f"expected a tensor, an int address or None, got {type(x)!r}")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _enum(value, names):
+    if isinstance(value, str):
+        return names[value]
+    return int(value)
+
+
+_LAYOUT_NAMES = {"kv": QLA_LAYOUT_KV, "vk": QLA_LAYOUT_VK}
+_DIR_NAMES = {"fwd": QLA_DIR_FWD, "bwd": QLA_DIR_BWD}
+
+
+def raw_correct_h0(H, M, S0, out, layout, direction, batch, heads, n_seg, K, V, stream=None,
+                   lib: ctypes.CDLL | None = None) -> int:
+    """Call qla_correct_h0 and return its status code unchanged."""
+    lib = lib or load_library()
+    return lib.qla_correct_h0(_ptr(H), _ptr(M), _ptr(S0), _ptr(out),
+                              _enum(layout, _LAYOUT_NAMES), _enum(direction, _DIR_NAMES),
+                              batch, heads, n_seg, K, V, _stream(stream))
+
+
+def qla_correct_h0(H, M, S0, out, layout, direction, batch, heads, n_seg, K, V, stream=None,
+                   lib: ctypes.CDLL | None = None) -> None:
+    """Enqueue the correction on ``stream`` (default: torch's current stream); raises QlaError."""
+    lib = lib or load_library()
+    rc = raw_correct_h0(H, M, S0, out, layout, direction, batch, heads, n_seg, K, V, stream, lib)
+    if rc != 0:
+        raise QlaError(rc, qla_status_str(rc, lib))
+
+
+def _groups(groups):
+    arr = (qla_head_group * max(len(groups), 1))()
+    for i, g in enumerate(groups):
+        begin, count, layout, direction = g
+        arr[i] = qla_head_group(begin, count, _enum(layout, _LAYOUT_NAMES), _enum(direction, _DIR_NAMES))
+    return arr
+
+
+def raw_correct_h0_grouped(H, M, S0, out, groups, batch, heads, n_seg, K, V, stream=None,
+                           lib: ctypes.CDLL | None = None, n_groups: int | None = None) -> int:
+    """Call qla_correct_h0_grouped; ``groups`` is a list of (head_begin, head_count, layout, direction)."""
+    lib = lib or load_library()
+    arr = _groups(groups)
+    n = len(groups) if n_groups is None else n_groups
+    return lib.qla_correct_h0_grouped(_ptr(H), _ptr(M), _ptr(S0), _ptr(out), arr, n,
+                                      batch, heads, n_seg, K, V, _stream(stream))
+
+
+def qla_correct_h0_grouped(H, M, S0, out, groups, batch, heads, n_seg, K, V, stream=None,
+                           lib: ctypes.CDLL | None = None) -> None:
+    lib = lib or load_library()
+    rc = raw_correct_h0_grouped(H, M, S0, out, groups, batch, heads, n_seg, K, V, stream, lib)
+    if rc != 0:
+        raise QlaError(rc, qla_status_str(rc, lib))

@@ -1,0 +1,41 @@
+// qla_internal.h -- declarations shared by the host entry points and the
+// kernel launchers of libqla.so (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+
+#include "qla.h"
+
+namespace qla {
+
+struct LaunchArgs {
+    const float* H;
+    const float* M;
+    const float* S0;  // may be null: zero initial state
+    float* out;
+    int layout;
+    int direction;
+    long long chains;  // batch * heads
+    int heads;
+    int n_seg;
+    int K;
+    int V;
+    void* stream;
+};
+
+// Head-group table copied by value into the grouped kernel's arguments.
+// variant = 2 * layout + direction.
+struct GroupTable {
+    int n;
+    int begin[QLA_MAX_GROUPS];
+    int count[QLA_MAX_GROUPS];
+    int variant[QLA_MAX_GROUPS];
+};
+
+int tiles_for(int V);
+hipError_t launch_correct_h0(const LaunchArgs& a);
+hipError_t launch_correct_h0_grouped(const LaunchArgs& a, const GroupTable& table);
+
+}  // namespace qla

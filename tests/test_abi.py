@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/qla.h declares, and rejects bad arguments before touching the
+HIP runtime.  Fake addresses used here are never dereferenced: each call fails
+an earlier check (enum, shape, groups, NULL, alignment, overlap)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_attention_context_amd as qla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(qla.library_path()) or not os.path.exists(qla.library_path("delay")):
+        from linear_attention_context_amd import build
+        build.build()
+    return qla.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"QLA_API\s+[\w\s\*]+?\b(qla_\w+)\s*\(", text)
+
+
+def test_header_declares_three_entry_points():
+    assert sorted(declared_functions()) == ["qla_correct_h0", "qla_correct_h0_grouped", "qla_status_str"]
+
+
+@pytest.mark.parametrize("variant", ["", "delay"])
+def test_library_exports_declared_symbols(lib, variant):
+    path = qla.library_path(variant)
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(declared_functions()) <= exported
+    # nothing else leaks out of the C ABI
+    assert all(name.startswith("qla_") for name in exported), exported
+
+
+def test_status_strings(lib):
+    for code, name in qla.STATUS.items():
+        s = qla.qla_status_str(code)
+        assert s and s != "unknown status", (code, name)
+    assert qla.qla_status_str(12345) == "unknown status"
+
+
+A = 0x10000000  # fake 16-byte aligned addresses, never dereferenced
+
+
+def call(**kw):
+    args = dict(H=A, M=A + 0x10000000, S0=None, out=A + 0x20000000, layout=0, direction=0,
+                batch=1, heads=2, n_seg=3, K=64, V=64, stream=0)
+    args.update(kw)
+    return qla.raw_correct_h0(**args)
+
+
+def test_enum_errors(lib):
+    assert call(layout=2) == -2
+    assert call(direction=-1) == -2
+
+
+@pytest.mark.parametrize("kw", [dict(K=96), dict(K=32), dict(V=6), dict(V=0), dict(V=4100),
+                                dict(batch=-1), dict(heads=-2), dict(n_seg=-1),
+                                dict(batch=2 ** 30, heads=2 ** 10)])
+def test_shape_errors(lib, kw):
+    assert call(**kw) == -3
+
+
+def test_empty_calls_return_ok_without_pointers(lib):
+    for kw in [dict(batch=0), dict(heads=0), dict(n_seg=0)]:
+        assert call(H=None, M=None, out=None, **kw) == 0
+
+
+def test_null_errors(lib):
+    assert call(H=None) == -1
+    assert call(M=None) == -1
+    assert call(out=None) == -1
+
+
+def test_alignment_errors(lib):
+    assert call(H=A + 4) == -4
+    assert call(out=A + 0x20000008) == -4
+    assert call(S0=A + 0x30000004) == -4
+
+
+def test_alias_errors(lib):
+    state = 64 * 64 * 4
+    hbytes = 2 * 3 * state
+    # out overlapping H but not identical
+    assert call(out=A + 16) == -5
+    # out overlapping M
+    assert call(out=A + 0x10000000 + 16) == -5
+    # out overlapping S0
+    assert call(S0=A + 0x20000000 + hbytes - 16) == -5
+
+
+def groups_call(groups, n_groups=None, heads=4, **kw):
+    args = dict(H=A, M=A + 0x10000000, S0=None, out=A + 0x20000000, groups=groups,
+                batch=1, heads=heads, n_seg=2, K=64, V=64, stream=0, n_groups=n_groups)
+    args.update(kw)
+    return qla.raw_correct_h0_grouped(**args)
+
+
+@pytest.mark.parametrize("groups", [
+    [(0, 2, "kv", "fwd"), (1, 3, "vk", "bwd")],        # overlap
+    [(0, 1, "kv", "fwd"), (2, 2, "vk", "bwd")],        # gap
+    [(0, 2, "kv", "fwd")],                             # does not cover
+    [(0, 5, "kv", "fwd")],                             # past heads
+    [(-1, 5, "kv", "fwd")],                            # negative begin
+    [(0, 0, "kv", "fwd"), (0, 4, "kv", "fwd")],        # empty group
+])
+def test_group_partition_errors(lib, groups):
+    assert groups_call(groups) == -6
+
+
+def test_group_count_limits(lib):
+    assert groups_call([(0, 4, "kv", "fwd")], n_groups=0) == -6
+    many = [(i, 1, "kv", "fwd") for i in range(65)]
+    assert groups_call(many, heads=65) == -6
+    assert groups_call([(0, 4, 3, 0)]) == -2
+
+
+def test_group_empty_call_ok(lib):
+    assert groups_call([(0, 4, "kv", "fwd")], H=None, M=None, out=None, n_seg=0) == 0
+
+
+def test_binding_raises_with_status(lib):
+    with pytest.raises(qla.QlaError) as e:
+        qla.qla_correct_h0(A, A + 0x10000000, None, A + 0x20000000, 0, 0, 1, 1, 1, 96, 64, stream=0)
+    assert e.value.status == -3
