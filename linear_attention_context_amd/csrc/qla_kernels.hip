@@ -55,21 +55,37 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 typedef unsigned u2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+#ifndef QLA_WAVES
+#define QLA_WAVES(K) ((K) >= 128 ? 8 : 4)
+#endif
 constexpr int kTileV = 16;  // kv-view columns per workgroup
+
+#ifndef QLA_PREFETCH_UNITS
+#define QLA_PREFETCH_UNITS(K) ((K) >= 256 ? 1 : (K) >= 128 ? 2 : 3)
+#endif
 
 template <int K>
 struct Shape {
-    static constexpr int ROWS = K / kWaves;       // output rows per wave
+    // Waves per workgroup: two per SIMD where the registers allow it, so
+    // that one wave's operand waits are covered by the other's MFMAs.
+    static constexpr int WAVES = QLA_WAVES(K);
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int ROWS = K / WAVES;        // output rows per wave
     static constexpr int T = ROWS / 16;           // 16-row MFMA tiles per wave
     static constexpr int KP = K >= 256 ? 64 : K;  // k-width of one M panel
     static constexpr int NP = K / KP;             // panels per step
     static constexpr int BP = KP / 16;            // 16-wide k blocks per panel
     static constexpr int LS = K + 4;              // LDS row stride (floats)
-    static constexpr int LDS_FLOATS = 2 * kTileV * LS;
+    static constexpr int STATE_FLOATS = 2 * kTileV * LS;  // two state slots
+    static constexpr int STAGE_FLOATS = ROWS * KP;          // one wave's M panel share
+    // Forward staging slots per wave: two (the next panel is written while
+    // this one is read) when they fit in the 160 KiB of LDS, else one.
+    static constexpr int SS = (STATE_FLOATS + WAVES * 2 * STAGE_FLOATS) * 4 <= 160 * 1024 ? 2 : 1;
+    static constexpr int RPI = 256 / KP;                    // M rows per coalesced load instruction
+    // Prefetch distance in panels (see Tile::prefetch).
+    static constexpr int D = QLA_PREFETCH_UNITS(K);
     static_assert(ROWS % 16 == 0, "K must be a multiple of 64");
-    static_assert(NP == 1 || NP % 2 == 0, "panel ring needs NP = 1 or even");
+    static_assert(NP <= 4, "at most four panels per step");
 };
 
 // Wait until this wave's LDS accesses are done, then meet the other waves.
@@ -136,12 +152,18 @@ struct Tile {
     static constexpr bool KV = LAYOUT == QLA_LAYOUT_KV;
     static constexpr bool FWD = DIR == QLA_DIR_FWD;
     static constexpr unsigned kMatBytes = (unsigned)K * K * 4u;
+    // LDS: two state slots, plus one M staging slot per wave when forward.
+    static constexpr int SS = S::SS;
+    static constexpr int SF = S::STAGE_FLOATS;
+    static constexpr int LDS_FLOATS = S::STATE_FLOATS + (FWD ? S::WAVES * SS * SF : 0);
 
     // Per-lane constants of one workgroup.
     struct Lane {
         int wave, g, c, a0;
         unsigned hoff[T];  // byte offsets of the lane's H/out vectors (kOutOfRange if masked)
-        unsigned moff;     // byte offset of the lane's first M operand
+        unsigned moff;     // byte offset of the lane's first M operand (backward)
+        unsigned mcoal;    // byte offset of the lane's first coalesced M chunk (forward)
+        int prot, brot;    // k-order rotation of this wave: panels, then 16-k blocks in a panel
         unsigned state_bytes;
     };
 
@@ -179,48 +201,41 @@ struct Tile {
             L.hoff[i] = valid ? 4u * (unsigned)e : kOutOfRange;
         }
         // Forward: M[a0 + c][4g]; backward: M[4g][a0 + T*c] (panel/block/tile offsets added per load).
-        L.moff = FWD ? 4u * (unsigned)((L.a0 + L.c) * K + 4 * L.g) : 4u * (unsigned)(4 * L.g * K + L.a0 + T * L.c);
+        L.moff = 4u * (unsigned)(4 * L.g * K + L.a0 + T * L.c);
+        // Each wave walks the k range starting at its own rows (k = a0 ...):
+        // the state of those rows is its own output, readable before the
+        // other waves have written theirs.
+        L.prot = (L.wave * S::ROWS / KP) % NP;
+        L.brot = (L.wave * S::ROWS / 16) % BP;
+        L.mcoal = 4u * (unsigned)((L.a0 + lane / (KP / 4)) * K + 4 * (lane % (KP / 4)));
         return L;
-    }
-
-    // Load panel p of one M matrix (this wave's share) into a ring slot.
-    static __device__ __forceinline__ void load_panel(f4 (&m)[T][BP], __amdgpu_buffer_rsrc_t Mr, int p,
-                                                      const Lane& L)
-    {
-        if (FWD) {
-            // operand (a, k) = M[a][k], a = a0 + 16t + c, k = p*KP + 16b + 4g + q: 16 bytes per (t, b).
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-#pragma unroll
-                for (int b = 0; b < BP; ++b)
-                    m[t][b] = bload4(Mr, L.moff + 4u * (unsigned)(16 * t * K + p * KP + 16 * b));
-        } else {
-            // Backward uses M^T: operand (a, k) = M[k][a], a = a0 + T*c + t.  The
-            // T tiles' values of one M row are adjacent: one T-wide load per (b, q).
-#pragma unroll
-            for (int b = 0; b < BP; ++b)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const unsigned off = L.moff + 4u * (unsigned)((p * KP + 16 * b + q) * K);
-                    if (T == 1) {
-                        m[0][b][q] = bload1(Mr, off);
-                    } else if (T == 2) {
-                        const f2 x = bload2(Mr, off);
-                        m[0][b][q] = x[0];
-                        m[T - 1][b][q] = x[1];
-                    } else {
-                        const f4 x = bload4(Mr, off);
-#pragma unroll
-                        for (int t = 0; t < T; ++t) m[t][b][q] = x[t & 3];
-                    }
-                }
-        }
     }
 
     static __device__ __forceinline__ void load_state(f4 (&h)[T], __amdgpu_buffer_rsrc_t r, const Lane& L)
     {
 #pragma unroll
         for (int i = 0; i < T; ++i) h[i] = bload4(r, L.hoff[i]);
+    }
+
+    // Forward M staging.  Each wave owns a private LDS slot of ROWS x KP
+    // floats, laid out [row][16-byte chunk] with the chunk index XORed by
+    // (row & 7) so that both the line-wise writes and the MFMA-layout reads
+    // (16 rows, same chunk) spread over all banks.  The slot is private to
+    // the wave and LDS executes one wave's accesses in order, so the next
+    // panel's writes cannot overtake this panel's reads: no barrier needed.
+    static __device__ __forceinline__ int stage_off(int row, int chunk) { return row * KP + 4 * (chunk ^ (row & 7)); }
+
+    // MFMA operand (a, k) = M[a0 + 16t + c][p*KP + 16b + 4g + q] for one (t, b).
+    static __device__ __forceinline__ f4 stage_read(const float* stage, int t, int b, const Lane& L)
+    {
+        return *reinterpret_cast<const f4*>(stage + stage_off(16 * t + L.c, 4 * ((b + L.brot) & (BP - 1)) + L.g));
+    }
+
+    // Position of k block (panel p, block b of the wave's walk) in the k range.
+    static __device__ __forceinline__ int panel_of(int p, const Lane& L) { return (p + L.prot) & (NP - 1); }
+    static __device__ __forceinline__ int kblock(int p, int b, const Lane& L)
+    {
+        return panel_of(p, L) * BP + ((b + L.brot) & (BP - 1));
     }
 
     // Write the lane's fragment of the state into one LDS slot ([v][k] order).
@@ -293,73 +308,274 @@ struct Tile {
 
     static __device__ __forceinline__ int seg(const Chain& C, int s) { return FWD ? s : C.n_seg - 1 - s; }
 
-    // One segment step.  PAR = s & 1 selects the register ring slots and the
-    // LDS state slot (read PAR, write PAR ^ 1).
-    template <int PAR>
-    static __device__ __forceinline__ void step(int s, const Chain& C, f4 (&m)[2][T][BP], f4 (&h)[2][T],
+    // Prefetch ring.  The M stream of a chain is a sequence of units (one
+    // panel of one step, NP units per step).  Unit u lives in register slot
+    // u % R and is loaded D = R - 1 units ahead of its use, into the slot the
+    // previous unit just freed.  H_j rides along with the first unit of its
+    // step, in slot (step % RH).  Step loops are unrolled by F so that every
+    // slot index is a compile-time constant.
+    static constexpr int D = S::D;
+    static constexpr int R = D + 1;
+    static constexpr int RH = (NP - 1 + D) / NP + 1;
+    static constexpr int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
+    static constexpr int F0 = R / gcd(R, NP);
+    static constexpr int F = F0 * RH / gcd(F0, RH);
+    static_assert(F >= 1 && F <= 6, "unroll block must be 1..6 steps");
+    static_assert(!(FWD && SS == 2) || D >= 2, "two-slot staging stages a unit loaded two units ahead");
+
+    // ---- one load / staging-write instruction at a time -------------------
+    // Loads of one M panel (this wave's share): forward, T*BP whole-line
+    // instructions (instruction i covers rows i*RPI .. i*RPI + RPI - 1 of the
+    // share); backward, 4*BP T-wide instructions (one per (b, q)).
+    static constexpr int kPanelLoads = FWD ? T * BP : 4 * BP;
+
+    template <int I>
+    static __device__ __forceinline__ void load_m(f4 (&m)[T][BP], __amdgpu_buffer_rsrc_t Mr, int panel, const Lane& L)
+    {
+        const int pa = panel_of(panel, L);
+        if constexpr (FWD) {
+            m[I / BP][I % BP] = bload4(Mr, L.mcoal + 4u * (unsigned)(I * S::RPI * K + pa * KP));
+        } else {
+            // operand (a, k) = M[k][a], a = a0 + T*c + t, k = 16*kblock + 4g + q
+            constexpr int b = I / 4, q = I % 4;
+            const unsigned off = L.moff + 4u * (unsigned)((pa * KP + 16 * ((b + L.brot) & (BP - 1)) + q) * K);
+            if constexpr (T == 1) {
+                m[0][b][q] = bload1(Mr, off);
+            } else if constexpr (T == 2) {
+                const f2 x = bload2(Mr, off);
+                m[0][b][q] = x[0];
+                m[1][b][q] = x[1];
+            } else {
+                const f4 x = bload4(Mr, off);
+#pragma unroll
+                for (int t = 0; t < T; ++t) m[t][b][q] = x[t];
+            }
+        }
+    }
+
+    // Forward staging write of register group I = t*BP + b of a panel share.
+    template <int I>
+    static __device__ __forceinline__ void stage_write_one(float* stage, const f4 (&m)[T][BP])
+    {
+        const int lane = threadIdx.x & 63;
+        const int row = I * S::RPI + lane / (KP / 4);
+        st4(stage + stage_off(row, lane % (KP / 4)), m[I / BP][I % BP]);
+    }
+
+    // Prefetch target of one panel: the unit D ahead.
+    struct Prefetch {
+        __amdgpu_buffer_rsrc_t Mr, Hr;
+        int panel;
+    };
+
+    // Issue prefetch loads [LO, HI) of the target unit: M instructions first,
+    // then (on a step's first panel) the T vectors of H.
+    template <int LO, int HI, int TLS, int TP>
+    static __device__ __forceinline__ void issue_loads(const Prefetch& pf, f4 (&m)[R][T][BP], f4 (&h)[RH][T],
+                                                       const Lane& L)
+    {
+        if constexpr (LO < HI) {
+            if constexpr (LO < kPanelLoads)
+                load_m<LO>(m[(TLS * NP + TP) % R], pf.Mr, pf.panel, L);
+            else
+                h[TLS % RH][LO - kPanelLoads] = bload4(pf.Hr, L.hoff[LO - kPanelLoads]);
+            issue_loads<LO + 1, HI, TLS, TP>(pf, m, h, L);
+        }
+    }
+
+    template <int LO, int HI>
+    static __device__ __forceinline__ void issue_writes(float* stage, const f4 (&m)[T][BP])
+    {
+        if constexpr (LO < HI) {
+            stage_write_one<LO>(stage, m);
+            issue_writes<LO + 1, HI>(stage, m);
+        }
+    }
+
+    // State operand of (panel P, block b): P[k][c], k = 16*kblock + 4g + q.
+    template <int P, int LO, int HI>
+    static __device__ __forceinline__ void read_pv(f4 (&pv)[K / 16], const float* cur, const Lane& L)
+    {
+        if constexpr (LO < HI) {
+            pv[P * BP + LO] = *reinterpret_cast<const f4*>(cur + L.c * LS + 16 * kblock(P, LO, L) + 4 * L.g);
+            read_pv<P, LO + 1, HI>(pv, cur, L);
+        }
+    }
+
+    // Working set of one step.
+    struct StepCtx {
+        f4 acc[T];
+        f4 pv[K / 16];
+        f4 mo[3][T];  // forward: staged M operand, read two blocks ahead
+        const float* cur;
+        const float* st_cur;
+        float* st_next;
+    };
+
+    // Blocks of a step, in the wave's k order: the first T blocks are the
+    // wave's own rows, whose state the wave wrote itself; the barrier that
+    // publishes the other waves' rows sits after the first of them, so its
+    // wait and the following state reads overlap the remaining own-row MFMAs.
+    static constexpr int kOwn = T;  // 16-k blocks of own rows
+    static constexpr int kOwnP0 = kOwn < BP ? kOwn : BP;
+
+    // One 16-k block B of panel P (local step LSX): half the block's MFMAs,
+    // staged reads two blocks ahead, this block's share of the prefetch loads
+    // and of the next panel's staging writes, the other half of the MFMAs.
+    // Each block is its own scheduling region so the CU's vector-memory and
+    // LDS work is spread through the matrix-core work.
+    template <int LSX, int P, int B>
+    static __device__ __forceinline__ void block(StepCtx& X, const Prefetch& pf, f4 (&m)[R][T][BP],
+                                                 f4 (&h)[RH][T], const Lane& L)
+    {
+        constexpr int slot = (LSX * NP + P) % R;
+        constexpr int TLS = LSX + (P + D) / NP, TP = (P + D) % NP;
+        constexpr int NL = kPanelLoads + (TP == 0 ? T : 0);
+        constexpr int l0 = NL * B / BP, l1 = NL * (B + 1) / BP;
+        constexpr int NW = (FWD && SS == 2) ? T * BP : 0;
+        constexpr int w0 = NW * B / BP, w1 = NW * (B + 1) / BP;
+        constexpr int nr = (FWD && B + 2 < BP) ? T : 0;
+
+        auto mfma = [&](int q) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const float pk = X.pv[P * BP + B][q];
+                const float mk = FWD ? X.mo[B % 3][t][q] : m[slot][t][B][q];
+                if (KV)
+                    X.acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(pk, mk, X.acc[t], 0, 0, 0);
+                else
+                    X.acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(mk, pk, X.acc[t], 0, 0, 0);
+            }
+        };
+        mfma(0);
+        mfma(1);
+        if constexpr (nr > 0) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) X.mo[(B + 2) % 3][t] = stage_read(X.st_cur, t, B + 2, L);
+        }
+        issue_loads<l0, l1, TLS, TP>(pf, m, h, L);
+        if constexpr (NW > 0) issue_writes<w0, w1>(X.st_next, m[(LSX * NP + P + 1) % R]);
+        mfma(2);
+        mfma(3);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * T, 0);                                // MFMA
+        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);             // DS read
+        if constexpr (l1 > l0) __builtin_amdgcn_sched_group_barrier(0x020, l1 - l0, 0);       // VMEM read
+        if constexpr (w1 > w0) __builtin_amdgcn_sched_group_barrier(0x200, w1 - w0, 0);       // DS write
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * T, 0);                                // MFMA
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (P == 0 && B == 0) {
+            // Publish / acquire the state rows of the other waves, then read
+            // their part of this panel's state operand.
+            lds_handoff();
+            read_pv<0, kOwnP0, BP>(X.pv, X.cur, L);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (B + 1 < BP) block<LSX, P, B + 1>(X, pf, m, h, L);
+    }
+
+    // Panel P of step s (local index LSX).
+    template <int LSX, int P>
+    static __device__ __forceinline__ void panel(int s, StepCtx& X, const Chain& C, f4 (&m)[R][T][BP],
+                                                 f4 (&h)[RH][T], float* stage, const Lane& L)
+    {
+        constexpr int slot = (LSX * NP + P) % R;
+        // Prefetch target: the unit D ahead, or an empty resource past the chain's end.
+        const int ts = s + (P + D) / NP;
+        const bool live = ts < C.n_seg;
+        const int tj = live ? seg(C, ts) : 0;
+        const Prefetch pf{rsrc(C.M + (size_t)tj * K * K, live ? kMatBytes : 0u),
+                          rsrc(C.H + (size_t)tj * (L.state_bytes / 4), live ? L.state_bytes : 0u), (P + D) % NP};
+        // Forward: this panel's M is read from staging slot (unit & 1),
+        // written during the previous panel (two slots) or just below (one).
+        // The next panel goes into the other slot, which the previous panel
+        // last read: this wave issued those reads before these writes, and LDS
+        // runs one wave's accesses in order.
+        const int unit = s * NP + P;
+        X.st_cur = stage + (SS == 2 ? (unit & 1) * SF : 0);
+        X.st_next = stage + (SS == 2 ? ((unit + 1) & 1) * SF : 0);
+
+        // State operand: panel 0's own-row blocks (own writes, no barrier
+        // needed); later panels after the barrier, in full.
+        if constexpr (P == 0) read_pv<0, 0, kOwnP0>(X.pv, X.cur, L);
+        else read_pv<P, 0, BP>(X.pv, X.cur, L);
+        if constexpr (FWD && SS == 1) issue_writes<0, T * BP>(stage, m[slot]);
+        if constexpr (FWD) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) X.mo[0][t] = stage_read(X.st_cur, t, 0, L);
+            if constexpr (BP > 1) {
+#pragma unroll
+                for (int t = 0; t < T; ++t) X.mo[1][t] = stage_read(X.st_cur, t, 1, L);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        block<LSX, P, 0>(X, pf, m, h, L);
+        if constexpr (P + 1 < NP) panel<LSX, P + 1>(s, X, C, m, h, stage, L);
+    }
+
+    // One segment step with compile-time local index LSX (position in the
+    // unrolled block).  Reads LDS state slot s & 1, writes slot (s + 1) & 1.
+    // Slot (s+1)&1 was last read during step s-1; every wave finished those
+    // reads before arriving at the barrier inside step s, and the writes come
+    // after it.  The other waves' rows of slot s&1 are read after that same
+    // barrier, which no wave reaches before its step s-1 writes landed.
+    template <int LSX>
+    static __device__ __forceinline__ void step(int s, const Chain& C, f4 (&m)[R][T][BP], f4 (&h)[RH][T],
                                                 float* lds, const Lane& L)
     {
         const int j = seg(C, s);
-        const bool more = s + 1 < C.n_seg;
-        const int jn = more ? seg(C, s + 1) : j;
-        const float* cur = lds + PAR * (kTileV * LS);
-        float* nxt = lds + (PAR ^ 1) * (kTileV * LS);
-        const __amdgpu_buffer_rsrc_t Mr = rsrc(C.M + (size_t)j * K * K, kMatBytes);
-        // Resources of the next step; empty after the last step, so its prefetch reads nothing.
-        const __amdgpu_buffer_rsrc_t Mn = rsrc(C.M + (size_t)jn * K * K, more ? kMatBytes : 0u);
-        const __amdgpu_buffer_rsrc_t Hn = rsrc(C.H + (size_t)jn * (L.state_bytes / 4), more ? L.state_bytes : 0u);
+        float* nxt = lds + ((s + 1) & 1) * (kTileV * LS);
+        float* stage = lds + S::STATE_FLOATS + L.wave * SS * SF;
 
-        f4 acc[T];
-#pragma unroll
-        for (int t = 0; t < T; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
-
+        __builtin_amdgcn_sched_barrier(0);
         debug_delay(L.wave, s, 0);
+        StepCtx X;
+        X.cur = lds + (s & 1) * (kTileV * LS);
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int slot = (PAR * NP + p) & 1;
-            // Prefetch the next panel (or the next step's first panel and H)
-            // into the other ring slot before computing on this one.
-            if (p + 1 < NP) {
-                load_panel(m[slot ^ 1], Mr, p + 1, L);
-            } else {
-                load_panel(m[slot ^ 1], Mn, 0, L);
-                load_state(h[PAR ^ 1], Hn, L);
-            }
-            // Keep the prefetch issued here, ahead of the MFMAs: left alone, the
-            // scheduler sinks the loads below them to save registers, which
-            // turns the prefetch into a stall at the next step.
-            __builtin_amdgcn_sched_barrier(0);
-            // Previous state, this panel's k range: P[k][c], k = p*KP + 16b + 4g + q.
-            f4 pv[BP];
-#pragma unroll
-            for (int b = 0; b < BP; ++b)
-                pv[b] = *reinterpret_cast<const f4*>(cur + L.c * LS + p * KP + 16 * b + 4 * L.g);
-#pragma unroll
-            for (int b = 0; b < BP; ++b)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int t = 0; t < T; ++t) {
-                        if (KV)
-                            acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[b][q], m[slot][t][b][q], acc[t], 0, 0, 0);
-                        else
-                            acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(m[slot][t][b][q], pv[b][q], acc[t], 0, 0, 0);
-                    }
-        }
+        for (int t = 0; t < T; ++t) X.acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+        panel<LSX, 0>(s, X, C, m, h, stage, L);
 
         // Correct: P = Y + X(H_j); emit out_j; hand the state to the next step.
         f4 hx[T];
-        frag_from_vecs(hx, h[PAR]);
+        frag_from_vecs(hx, h[LSX % RH]);
 #pragma unroll
-        for (int t = 0; t < T; ++t) acc[t] += hx[t];
+        for (int t = 0; t < T; ++t) X.acc[t] += hx[t];
         f4 ov[T];
-        vecs_from_frag(ov, acc);
+        vecs_from_frag(ov, X.acc);
         const __amdgpu_buffer_rsrc_t Or = rsrc(C.out + (size_t)j * (L.state_bytes / 4), L.state_bytes);
 #pragma unroll
         for (int i = 0; i < T; ++i) bstore4(Or, L.hoff[i], ov[i]);
         debug_delay(L.wave, s, 1);
-        put_state(nxt, acc, L);
-        lds_handoff();
+        put_state(nxt, X.acc, L);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Remaining steps after the unrolled loop (fewer than F), straight-line.
+    template <int LSX>
+    static __device__ __forceinline__ void tail(int s, int rem, const Chain& C, f4 (&m)[R][T][BP],
+                                                f4 (&h)[RH][T], float* lds, const Lane& L)
+    {
+        if constexpr (LSX < F - 1) {
+            if (rem > LSX) {
+                step<LSX>(s + LSX, C, m, h, lds, L);
+                tail<LSX + 1>(s, rem, C, m, h, lds, L);
+            }
+        }
+    }
+
+    // Prologue loads: units 0 .. D-1 (and the H of the steps they start).
+    template <int V_>
+    static __device__ __forceinline__ void prologue(const Chain& C, f4 (&m)[R][T][BP], f4 (&h)[RH][T],
+                                                    const Lane& L)
+    {
+        if constexpr (V_ < D) {
+            constexpr int TLS = V_ / NP, TP = V_ % NP;
+            const bool live = TLS < C.n_seg;
+            const int tj = live ? seg(C, TLS) : 0;
+            const Prefetch pf{rsrc(C.M + (size_t)tj * K * K, live ? kMatBytes : 0u),
+                              rsrc(C.H + (size_t)tj * (L.state_bytes / 4), live ? L.state_bytes : 0u), TP};
+            issue_loads<0, kPanelLoads + (TP == 0 ? T : 0), TLS, TP>(pf, m, h, L);
+            prologue<V_ + 1>(C, m, h, L);
+        }
     }
 
     static __device__ __forceinline__ void run(const float* H, const float* M, const float* S0, float* out,
@@ -370,27 +586,29 @@ struct Tile {
         const Chain C{M + chain * (size_t)n_seg * K * K, H + chain * state * n_seg, out + chain * state * n_seg,
                       n_seg};
 
-        f4 m[2][T][BP];
-        f4 h[2][T];
-        // Prologue: the first step's first panel and local state, then the
+        f4 m[R][T][BP];
+        f4 h[RH][T];
+        // Prologue: the first D units of M (and their steps' H), then the
         // initial state into LDS slot 0.
-        const int j0 = seg(C, 0);
-        load_panel(m[0], rsrc(C.M + (size_t)j0 * K * K, kMatBytes), 0, L);
-        load_state(h[0], rsrc(C.H + (size_t)j0 * state, L.state_bytes), L);
+        prologue<0>(C, m, h, L);
+        if constexpr (FWD && SS == 2) issue_writes<0, T * BP>(lds + S::STATE_FLOATS + L.wave * SS * SF, m[0]);
         {
             f4 sv[T], sx[T];
             load_state(sv, rsrc(S0 ? S0 + chain * state : H, S0 ? L.state_bytes : 0u), L);
             frag_from_vecs(sx, sv);
             put_state(lds, sx, L);
         }
-        lds_handoff();
 
         int s = 0;
-        for (; s + 1 < n_seg; s += 2) {
+        for (; s + F <= n_seg; s += F) {
             step<0>(s, C, m, h, lds, L);
-            step<1>(s + 1, C, m, h, lds, L);
+            if constexpr (F > 1) step<1 % F>(s + 1, C, m, h, lds, L);
+            if constexpr (F > 2) step<2 % F>(s + 2, C, m, h, lds, L);
+            if constexpr (F > 3) step<3 % F>(s + 3, C, m, h, lds, L);
+            if constexpr (F > 4) step<4 % F>(s + 4, C, m, h, lds, L);
+            if constexpr (F > 5) step<5 % F>(s + 5, C, m, h, lds, L);
         }
-        if (s < n_seg) step<0>(s, C, m, h, lds, L);
+        tail<0>(s, n_seg - s, C, m, h, lds, L);
     }
 };
 
@@ -405,11 +623,11 @@ __device__ __forceinline__ int xcd_logical_id(int b, int G)
 }
 
 template <int K, int LAYOUT, int DIR>
-__global__ __launch_bounds__(kThreads) void correct_h0_kernel(const float* H, const float* __restrict__ M,
+__global__ __launch_bounds__(Shape<K>::THREADS) void correct_h0_kernel(const float* H, const float* __restrict__ M,
                                                               const float* S0, float* out, int n_seg, int V,
                                                               int tiles)
 {
-    __shared__ __attribute__((aligned(16))) float lds[Shape<K>::LDS_FLOATS];
+    __shared__ __attribute__((aligned(16))) float lds[Tile<K, LAYOUT, DIR>::LDS_FLOATS];
     const int id = xcd_logical_id(blockIdx.x, gridDim.x);
     const int chain = id / tiles;
     const int tile = id - chain * tiles;
@@ -417,12 +635,12 @@ __global__ __launch_bounds__(kThreads) void correct_h0_kernel(const float* H, co
 }
 
 template <int K>
-__global__ __launch_bounds__(kThreads) void correct_h0_grouped_kernel(const float* H, const float* __restrict__ M,
+__global__ __launch_bounds__(Shape<K>::THREADS) void correct_h0_grouped_kernel(const float* H, const float* __restrict__ M,
                                                                       const float* S0, float* out, int n_seg,
                                                                       int V, int tiles, int heads,
                                                                       GroupTable table)
 {
-    __shared__ __attribute__((aligned(16))) float lds[Shape<K>::LDS_FLOATS];
+    __shared__ __attribute__((aligned(16))) float lds[Tile<K, QLA_LAYOUT_KV, QLA_DIR_FWD>::LDS_FLOATS];
     const int id = xcd_logical_id(blockIdx.x, gridDim.x);
     const int chain = id / tiles;
     const int tile = id - chain * tiles;
@@ -443,7 +661,7 @@ hipError_t launch_one(const LaunchArgs& a)
 {
     const int tiles = (a.V + kTileV - 1) / kTileV;
     const dim3 grid((unsigned)(a.chains * tiles));
-    hipLaunchKernelGGL((correct_h0_kernel<K, LAYOUT, DIR>), grid, dim3(kThreads), 0, (hipStream_t)a.stream, a.H,
+    hipLaunchKernelGGL((correct_h0_kernel<K, LAYOUT, DIR>), grid, dim3(Shape<K>::THREADS), 0, (hipStream_t)a.stream, a.H,
                        a.M, a.S0, a.out, a.n_seg, a.V, tiles);
     return hipGetLastError();
 }
@@ -463,7 +681,7 @@ hipError_t launch_grouped_k(const LaunchArgs& a, const GroupTable& table)
 {
     const int tiles = (a.V + kTileV - 1) / kTileV;
     const dim3 grid((unsigned)(a.chains * tiles));
-    hipLaunchKernelGGL((correct_h0_grouped_kernel<K>), grid, dim3(kThreads), 0, (hipStream_t)a.stream, a.H, a.M,
+    hipLaunchKernelGGL((correct_h0_grouped_kernel<K>), grid, dim3(Shape<K>::THREADS), 0, (hipStream_t)a.stream, a.H, a.M,
                        a.S0, a.out, a.n_seg, a.V, tiles, a.heads, table);
     return hipGetLastError();
 }
