@@ -8,10 +8,15 @@ N(0,1)), already resident in HBM when timing starts.  Each call in a step reads
 its own buffers, and steps rotate over enough buffer sets (> 256 MB MALL) that
 every call streams its inputs from HBM.
 
+Timing: the steps' kv calls run back to back, then their vk calls, with HIP
+events on the launch stream at the boundaries (--mode direct, default).
+--mode graph follows the pages' protocol instead: each variant's launches are
+captured in hipGraphs of 16 calls and replayed.
+
 Prints one JSON line.  value = corrections/s of the whole job; roofline =
-the dominant kernel's achieved TFLOP/s (its average launch duration from HIP
-events recorded on the launch stream) against the fp32 matrix peak;
-cpu_baseline = the fp64 oracle on the host, one thread, on the same workload.
+the dominant kernel's achieved TFLOP/s (its average launch duration from those
+events) against the fp32 matrix peak; cpu_baseline = the fp64 oracle on the
+host, one thread, on the same workload.
 """
 from __future__ import annotations
 
@@ -39,8 +44,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "correct_h0_kv_fwd_32k32h_traffic.
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=320)
+    p.add_argument("--warmup", type=int, default=32)
+    p.add_argument("--mode", choices=("direct", "graph"), default="direct",
+                   help="direct launches (default) or replays of captured hipGraphs")
+    p.add_argument("--graph-calls", type=int, default=16, help="launches per captured graph (--mode graph)")
     p.add_argument("--rotate", type=int, default=4, help="buffer sets cycled by the steps")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -80,6 +88,7 @@ def main(argv=None):
     import linear_attention_context_amd as qla
     import qla_inputs as qi
 
+    qla.load_library()  # fail loudly before anything else if the library is missing
     case = qi.CASES[2]
     B, NH, N, K, V = case.batch, case.heads, case.n_seg, case.K, case.V
     variants = [("kv", "fwd"), ("vk", "fwd")]
@@ -102,38 +111,85 @@ def main(argv=None):
         sets.append(calls)
     torch.cuda.synchronize()
 
-    def launch(c):
+    def launch(c, stream_handle):
         qla.qla_correct_h0(c["H"], c["M"], c["S0"], c["out"], c["layout"], c["direction"], B, NH, N, K, V,
-                           stream=stream.cuda_stream)
+                           stream=stream_handle)
 
-    for i in range(args.warmup):
-        for c in sets[i % args.rotate]:
-            launch(c)
-    torch.cuda.synchronize()
-
-    # Timed region: K steps, an event pair around every launch (on the launch stream).
     nv = len(variants)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nv)]
-          for _ in range(args.steps)]
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    for i in range(2 * args.rotate):  # first launches load the code objects
+        for c in sets[i % args.rotate]:
+            launch(c, stream.cuda_stream)
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_begin.record(stream)
-    for i in range(args.steps):
-        for v, c in enumerate(sets[i % args.rotate]):
-            ev[i][v][0].record(stream)
-            launch(c)
-            ev[i][v][1].record(stream)
-    t_end.record(stream)
+
+    # Host cost of one direct call (context): back to back, after warm-up.
+    nd = 64
+    w0 = time.perf_counter()
+    for i in range(nd):
+        launch(sets[i % args.rotate][0], stream.cuda_stream)
+    host_us = (time.perf_counter() - w0) / nd * 1e6
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    gpu_ms = t_begin.elapsed_time(t_end)
+
+    if args.mode == "graph":
+        # The pages' protocol: each variant's launches captured in a hipGraph
+        # of G calls (rotating buffer sets), replayed alternately with HIP
+        # events between replays on the launch stream.
+        G = args.graph_calls
+        if args.steps % G or args.warmup % G:
+            raise SystemExit(f"--steps and --warmup must be multiples of --graph-calls ({G})")
+        graphs = []
+        cap = torch.cuda.Stream()
+        for v in range(nv):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap, capture_error_mode="relaxed"):
+                h = torch.cuda.current_stream().cuda_stream
+                for i in range(G):
+                    launch(sets[i % args.rotate][v], h)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup // G):
+            for g in graphs:
+                g.replay()
+        torch.cuda.synchronize()
+        reps = args.steps // G
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps * nv + 1)]
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        ev[0].record(stream)
+        for r in range(reps):
+            for v, g in enumerate(graphs):
+                g.replay()
+                ev[r * nv + v + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        gpu_ms = ev[0].elapsed_time(ev[-1])
+        per_launch = {v: np.array([ev[r * nv + v].elapsed_time(ev[r * nv + v + 1]) for r in range(reps)]) * 1e3 / G
+                      for v in range(nv)}
+        timing = f"hipGraph of {G} launches per variant, replayed alternately; events between replays"
+    else:
+        # Direct launches on the stream: the steps' kv calls back to back, then
+        # their vk calls (same work as interleaving them), each run of K calls
+        # bracketed by HIP events on the launch stream; rotating buffer sets.
+        for i in range(args.warmup):
+            for c in sets[i % args.rotate]:
+                launch(c, stream.cuda_stream)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nv + 1)]
+        wall0 = time.perf_counter()
+        ev[0].record(stream)
+        for v in range(nv):
+            for i in range(args.steps):
+                launch(sets[i % args.rotate][v], stream.cuda_stream)
+            ev[v + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        gpu_ms = ev[0].elapsed_time(ev[-1])
+        per_launch = {v: np.array([ev[v].elapsed_time(ev[v + 1]) * 1e3 / args.steps]) for v in range(nv)}
+        timing = "direct launches, each variant's K calls back to back between HIP events"
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
 
     per_call_us = {}
     for v, (layout, direction) in enumerate(variants):
-        d = np.array([ev[i][v][0].elapsed_time(ev[i][v][1]) for i in range(args.steps)]) * 1e3
+        d = per_launch[v]
         per_call_us[f"{layout}_{direction}"] = {"mean": float(d.mean()), "median": float(np.median(d)),
                                                "min": float(d.min()), "max": float(d.max())}
 
@@ -163,7 +219,8 @@ def main(argv=None):
         "config": {"workload": "32K tokens x 32 heads: batch 1, 8 CP segments of 4096, K=V=128, forward, "
                                "kv and vk layouts (one call each per step)",
                    "batch": B, "heads": NH, "n_seg": N, "K": K, "V": V,
-                   "calls_per_step": [f"{l}_{d}" for l, d in variants], "buffer_sets": args.rotate},
+                   "calls_per_step": [f"{l}_{d}" for l, d in variants], "buffer_sets": args.rotate,
+                   "timing": timing},
         "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_FP32_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_FP32_MFMA_TFLOPS,
                      "traffic": read_traffic(), "kernel": f"correct_h0_kernel<128,{dominant}>",
@@ -171,21 +228,23 @@ def main(argv=None):
                      "hbm_gbps": hbm_gbps, "hbm_frac": hbm_gbps / PEAK_HBM_GBPS,
                      "roofline_frac_of_max_bound": t_roof / t_dom},
         "per_call_us": per_call_us,
+        "host_us_per_call": host_us,
         "kernel_source_sha256_16": kernel_source_hash(),
     }
 
     if not args.no_check:
-        # In-situ check: outputs written by the timed launches against the oracle.
+        # In-situ check: every output buffer written by the timed graph replays
+        # against the oracle.
         import oracle
-        last = sets[(args.steps - 1) % args.rotate]
         worst = 0.0
-        for c in last:
-            Hl, Sl = host[c["layout"]]
-            ref = oracle.correct_h0(Hl, M, Sl, c["layout"], c["direction"])
-            got = c["out"].cpu().numpy().astype(np.float64)
-            num = np.sqrt(((got - ref) ** 2).sum(axis=(-1, -2)))
+        for v, (layout, direction) in enumerate(variants):
+            Hl, Sl = host[layout]
+            ref = oracle.correct_h0(Hl, M, Sl, layout, direction)
             den = np.sqrt((ref ** 2).sum(axis=(-1, -2)))
-            worst = max(worst, float((num / den).max()))
+            for r in range(args.rotate):
+                got = sets[r][v]["out"].cpu().numpy().astype(np.float64)
+                num = np.sqrt(((got - ref) ** 2).sum(axis=(-1, -2)))
+                worst = max(worst, float((num / den).max()))
         result["timed_output_max_rel_l2"] = worst
         if not worst <= 2e-5:
             print(json.dumps(result))

@@ -55,35 +55,58 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 typedef unsigned u2 __attribute__((ext_vector_type(2)));
 
-#ifndef QLA_WAVES
-#define QLA_WAVES(K) ((K) >= 128 ? 8 : 4)
+#ifndef QLA_LDS_PAD
+#define QLA_LDS_PAD 8
+#endif
+#ifndef QLA_MLOAD_AUX
+#define QLA_MLOAD_AUX 0
+#endif
+#ifndef QLA_HLOAD_AUX
+#define QLA_HLOAD_AUX 0
+#endif
+#ifndef QLA_STORE_AUX
+#define QLA_STORE_AUX 2  // non-temporal: out is not re-read
+#endif
+#ifndef QLA_BARRIER_FIRST
+#define QLA_BARRIER_FIRST 0
 #endif
 constexpr int kTileV = 16;  // kv-view columns per workgroup
 
+// Waves per workgroup.  Forward at K >= 128 runs two waves per SIMD, so one
+// wave's operand waits are covered by the other's MFMAs.  Backward keeps
+// four: its M share is a column block, and 32 columns per wave make each
+// load a whole 128-byte line per row (16 columns would halve that).  The
+// grouped kernel has one block size for all its groups and uses eight.
+#ifndef QLA_WAVES
+#define QLA_WAVES(K, FWD) ((K) >= 128 && (FWD) ? 8 : 4)
+#endif
+#ifndef QLA_GROUPED_WAVES
+#define QLA_GROUPED_WAVES(K) ((K) >= 128 ? 8 : 4)
+#endif
+// Prefetch distance in units (panels) of M.
 #ifndef QLA_PREFETCH_UNITS
-#define QLA_PREFETCH_UNITS(K) ((K) >= 256 ? 1 : (K) >= 128 ? 2 : 3)
+#define QLA_PREFETCH_UNITS(K, FWD) ((K) >= 256 ? 1 : (K) >= 128 ? ((FWD) ? 3 : 2) : 3)
 #endif
 
-template <int K>
+template <int K, int WAVES_, bool FWD_>
 struct Shape {
-    // Waves per workgroup: two per SIMD where the registers allow it, so
-    // that one wave's operand waits are covered by the other's MFMAs.
-    static constexpr int WAVES = QLA_WAVES(K);
+    static constexpr int WAVES = WAVES_;
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int ROWS = K / WAVES;        // output rows per wave
     static constexpr int T = ROWS / 16;           // 16-row MFMA tiles per wave
     static constexpr int KP = K >= 256 ? 64 : K;  // k-width of one M panel
     static constexpr int NP = K / KP;             // panels per step
     static constexpr int BP = KP / 16;            // 16-wide k blocks per panel
-    static constexpr int LS = K + 4;              // LDS row stride (floats)
+    static constexpr int LS = K + QLA_LDS_PAD;    // LDS row stride (floats)
     static constexpr int STATE_FLOATS = 2 * kTileV * LS;  // two state slots
     static constexpr int STAGE_FLOATS = ROWS * KP;          // one wave's M panel share
     // Forward staging slots per wave: two (the next panel is written while
     // this one is read) when they fit in the 160 KiB of LDS, else one.
-    static constexpr int SS = (STATE_FLOATS + WAVES * 2 * STAGE_FLOATS) * 4 <= 160 * 1024 ? 2 : 1;
+    static constexpr int SS =
+        (STATE_FLOATS + WAVES * 2 * STAGE_FLOATS) * 4 <= 160 * 1024 && QLA_PREFETCH_UNITS(K, FWD_) >= 2 ? 2 : 1;
     static constexpr int RPI = 256 / KP;                    // M rows per coalesced load instruction
     // Prefetch distance in panels (see Tile::prefetch).
-    static constexpr int D = QLA_PREFETCH_UNITS(K);
+    static constexpr int D = QLA_PREFETCH_UNITS(K, FWD_);
     static_assert(ROWS % 16 == 0, "K must be a multiple of 64");
     static_assert(NP <= 4, "at most four panels per step");
 };
@@ -109,21 +132,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const float* base, unsign
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)bytes, kRsrcWord3);
 }
+template <int AUX = 0>
 __device__ __forceinline__ f4 bload4(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
-    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
 }
+template <int AUX = 0>
 __device__ __forceinline__ f2 bload2(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
-    return __builtin_bit_cast(f2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    return __builtin_bit_cast(f2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, AUX));
 }
+template <int AUX = 0>
 __device__ __forceinline__ float bload1(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, AUX));
 }
 __device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, unsigned off, f4 v)
 {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, (int)off, 0, QLA_STORE_AUX);
 }
 __device__ __forceinline__ void st4(float* p, f4 v) { *reinterpret_cast<f4*>(p) = v; }
 __device__ __forceinline__ void st2(float* p, f2 v) { *reinterpret_cast<f2*>(p) = v; }
@@ -145,9 +171,9 @@ __device__ __forceinline__ void debug_delay(int wave, int s, int which)
 #endif
 }
 
-template <int K, int LAYOUT, int DIR>
+template <int K, int LAYOUT, int DIR, int WAVES>
 struct Tile {
-    using S = Shape<K>;
+    using S = Shape<K, WAVES, DIR == QLA_DIR_FWD>;
     static constexpr int T = S::T, KP = S::KP, NP = S::NP, BP = S::BP, LS = S::LS;
     static constexpr bool KV = LAYOUT == QLA_LAYOUT_KV;
     static constexpr bool FWD = DIR == QLA_DIR_FWD;
@@ -219,11 +245,11 @@ struct Tile {
 
     // Forward M staging.  Each wave owns a private LDS slot of ROWS x KP
     // floats, laid out [row][16-byte chunk] with the chunk index XORed by
-    // (row & 7) so that both the line-wise writes and the MFMA-layout reads
+    // (row & 15) so that both the line-wise writes and the MFMA-layout reads
     // (16 rows, same chunk) spread over all banks.  The slot is private to
     // the wave and LDS executes one wave's accesses in order, so the next
     // panel's writes cannot overtake this panel's reads: no barrier needed.
-    static __device__ __forceinline__ int stage_off(int row, int chunk) { return row * KP + 4 * (chunk ^ (row & 7)); }
+    static __device__ __forceinline__ int stage_off(int row, int chunk) { return row * KP + 4 * (chunk ^ (row & 15)); }
 
     // MFMA operand (a, k) = M[a0 + 16t + c][p*KP + 16b + 4g + q] for one (t, b).
     static __device__ __forceinline__ f4 stage_read(const float* stage, int t, int b, const Lane& L)
@@ -334,19 +360,19 @@ struct Tile {
     {
         const int pa = panel_of(panel, L);
         if constexpr (FWD) {
-            m[I / BP][I % BP] = bload4(Mr, L.mcoal + 4u * (unsigned)(I * S::RPI * K + pa * KP));
+            m[I / BP][I % BP] = bload4<QLA_MLOAD_AUX>(Mr, L.mcoal + 4u * (unsigned)(I * S::RPI * K + pa * KP));
         } else {
             // operand (a, k) = M[k][a], a = a0 + T*c + t, k = 16*kblock + 4g + q
             constexpr int b = I / 4, q = I % 4;
             const unsigned off = L.moff + 4u * (unsigned)((pa * KP + 16 * ((b + L.brot) & (BP - 1)) + q) * K);
             if constexpr (T == 1) {
-                m[0][b][q] = bload1(Mr, off);
+                m[0][b][q] = bload1<QLA_MLOAD_AUX>(Mr, off);
             } else if constexpr (T == 2) {
-                const f2 x = bload2(Mr, off);
+                const f2 x = bload2<QLA_MLOAD_AUX>(Mr, off);
                 m[0][b][q] = x[0];
                 m[1][b][q] = x[1];
             } else {
-                const f4 x = bload4(Mr, off);
+                const f4 x = bload4<QLA_MLOAD_AUX>(Mr, off);
 #pragma unroll
                 for (int t = 0; t < T; ++t) m[t][b][q] = x[t];
             }
@@ -378,7 +404,7 @@ struct Tile {
             if constexpr (LO < kPanelLoads)
                 load_m<LO>(m[(TLS * NP + TP) % R], pf.Mr, pf.panel, L);
             else
-                h[TLS % RH][LO - kPanelLoads] = bload4(pf.Hr, L.hoff[LO - kPanelLoads]);
+                h[TLS % RH][LO - kPanelLoads] = bload4<QLA_HLOAD_AUX>(pf.Hr, L.hoff[LO - kPanelLoads]);
             issue_loads<LO + 1, HI, TLS, TP>(pf, m, h, L);
         }
     }
@@ -463,7 +489,7 @@ struct Tile {
         if constexpr (w1 > w0) __builtin_amdgcn_sched_group_barrier(0x200, w1 - w0, 0);       // DS write
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * T, 0);                                // MFMA
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (P == 0 && B == 0) {
+        if constexpr (P == 0 && B == 0 && !QLA_BARRIER_FIRST) {
             // Publish / acquire the state rows of the other waves, then read
             // their part of this panel's state operand.
             lds_handoff();
@@ -506,6 +532,10 @@ struct Tile {
 #pragma unroll
                 for (int t = 0; t < T; ++t) X.mo[1][t] = stage_read(X.st_cur, t, 1, L);
             }
+        }
+        if constexpr (P == 0 && QLA_BARRIER_FIRST) {
+            lds_handoff();
+            read_pv<0, kOwnP0, BP>(X.pv, X.cur, L);
         }
         __builtin_amdgcn_sched_barrier(0);
         block<LSX, P, 0>(X, pf, m, h, L);
@@ -623,24 +653,32 @@ __device__ __forceinline__ int xcd_logical_id(int b, int G)
 }
 
 template <int K, int LAYOUT, int DIR>
-__global__ __launch_bounds__(Shape<K>::THREADS) void correct_h0_kernel(const float* H, const float* __restrict__ M,
-                                                              const float* S0, float* out, int n_seg, int V,
-                                                              int tiles)
+struct Plain {
+    static constexpr int WAVES = QLA_WAVES(K, DIR == QLA_DIR_FWD);
+    using Tl = Tile<K, LAYOUT, DIR, WAVES>;
+};
+
+template <int K, int LAYOUT, int DIR>
+__global__ __launch_bounds__(64 * QLA_WAVES(K, DIR == QLA_DIR_FWD)) void correct_h0_kernel(
+    const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles)
 {
-    __shared__ __attribute__((aligned(16))) float lds[Tile<K, LAYOUT, DIR>::LDS_FLOATS];
+    using Tl = typename Plain<K, LAYOUT, DIR>::Tl;
+    __shared__ __attribute__((aligned(16))) float lds[Tl::LDS_FLOATS];
     const int id = xcd_logical_id(blockIdx.x, gridDim.x);
     const int chain = id / tiles;
     const int tile = id - chain * tiles;
-    Tile<K, LAYOUT, DIR>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds);
+    Tl::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds);
 }
 
 template <int K>
-__global__ __launch_bounds__(Shape<K>::THREADS) void correct_h0_grouped_kernel(const float* H, const float* __restrict__ M,
-                                                                      const float* S0, float* out, int n_seg,
-                                                                      int V, int tiles, int heads,
-                                                                      GroupTable table)
+__global__ __launch_bounds__(64 * QLA_GROUPED_WAVES(K)) void correct_h0_grouped_kernel(
+    const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles, int heads,
+    GroupTable table)
 {
-    __shared__ __attribute__((aligned(16))) float lds[Tile<K, QLA_LAYOUT_KV, QLA_DIR_FWD>::LDS_FLOATS];
+    constexpr int W = QLA_GROUPED_WAVES(K);
+    constexpr int F1 = Tile<K, QLA_LAYOUT_KV, QLA_DIR_FWD, W>::LDS_FLOATS;
+    constexpr int F2 = Tile<K, QLA_LAYOUT_KV, QLA_DIR_BWD, W>::LDS_FLOATS;
+    __shared__ __attribute__((aligned(16))) float lds[F1 > F2 ? F1 : F2];
     const int id = xcd_logical_id(blockIdx.x, gridDim.x);
     const int chain = id / tiles;
     const int tile = id - chain * tiles;
@@ -649,10 +687,10 @@ __global__ __launch_bounds__(Shape<K>::THREADS) void correct_h0_grouped_kernel(c
     for (int i = 0; i < table.n; ++i)
         if (head >= table.begin[i] && head < table.begin[i] + table.count[i]) variant = table.variant[i];
     switch (variant) {
-    case 0: Tile<K, QLA_LAYOUT_KV, QLA_DIR_FWD>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
-    case 1: Tile<K, QLA_LAYOUT_KV, QLA_DIR_BWD>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
-    case 2: Tile<K, QLA_LAYOUT_VK, QLA_DIR_FWD>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
-    default: Tile<K, QLA_LAYOUT_VK, QLA_DIR_BWD>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
+    case 0: Tile<K, QLA_LAYOUT_KV, QLA_DIR_FWD, W>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
+    case 1: Tile<K, QLA_LAYOUT_KV, QLA_DIR_BWD, W>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
+    case 2: Tile<K, QLA_LAYOUT_VK, QLA_DIR_FWD, W>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
+    default: Tile<K, QLA_LAYOUT_VK, QLA_DIR_BWD, W>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
     }
 }
 
@@ -661,7 +699,8 @@ hipError_t launch_one(const LaunchArgs& a)
 {
     const int tiles = (a.V + kTileV - 1) / kTileV;
     const dim3 grid((unsigned)(a.chains * tiles));
-    hipLaunchKernelGGL((correct_h0_kernel<K, LAYOUT, DIR>), grid, dim3(Shape<K>::THREADS), 0, (hipStream_t)a.stream, a.H,
+    hipLaunchKernelGGL((correct_h0_kernel<K, LAYOUT, DIR>), grid, dim3(64 * Plain<K, LAYOUT, DIR>::WAVES), 0,
+                       (hipStream_t)a.stream, a.H,
                        a.M, a.S0, a.out, a.n_seg, a.V, tiles);
     return hipGetLastError();
 }
@@ -681,7 +720,8 @@ hipError_t launch_grouped_k(const LaunchArgs& a, const GroupTable& table)
 {
     const int tiles = (a.V + kTileV - 1) / kTileV;
     const dim3 grid((unsigned)(a.chains * tiles));
-    hipLaunchKernelGGL((correct_h0_grouped_kernel<K>), grid, dim3(Shape<K>::THREADS), 0, (hipStream_t)a.stream, a.H, a.M,
+    hipLaunchKernelGGL((correct_h0_grouped_kernel<K>), grid, dim3(64 * QLA_GROUPED_WAVES(K)), 0, (hipStream_t)a.stream,
+                       a.H, a.M,
                        a.S0, a.out, a.n_seg, a.V, tiles, a.heads, table);
     return hipGetLastError();
 }

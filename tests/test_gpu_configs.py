@@ -6,7 +6,8 @@ Sizes (batch x heads x segments, K = V):
   3: as 2, bwd kv and vk             -- oracle on every state
   4: 4 x 32 x 64, 128, fwd kv        -- oracle on sampled chains
   5: 2 x 64 x 16, 256, one grouped call, four head groups -- oracle on sampled chains,
-     grouped == per-group calls bit for bit on every chain
+     grouped agrees with the per-group plain calls on every chain (parity bar),
+     and repeated grouped calls are bit-identical
 """
 import numpy as np
 import pytest
@@ -79,7 +80,9 @@ def test_config5_grouped():
             ref = oracle.correct_h0(H[b, h], M[b, h], S0[b, h], layout, direction)
             worst = assert_parity(got[b, h], ref, f"config 5 chain ({b},{h}) {layout} {direction}")
             print(f"  config 5 chain ({b},{h}) {layout} {direction}: max rel L2 {worst:.3e}", flush=True)
-    # every chain: grouped launch == the plain entry point on that group's heads
+    # every chain: the grouped launch agrees with the plain entry point on that
+    # group's heads.  The two may run a group with different wave counts, and so
+    # different fp32 summation orders: agreement is to the parity bar, not bits.
     import torch
 
     import linear_attention_context_amd as qla
@@ -90,7 +93,27 @@ def test_config5_grouped():
             qla.qla_correct_h0(Hd[b, sl], Md[b, sl], Sd[b, sl], sep, layout, direction, 1, count,
                                case.n_seg, case.K, case.V)
             torch.cuda.synchronize()
-            assert torch.equal(sep.view(torch.int32), out[b, sl].view(torch.int32)), (b, begin)
+            assert_parity(out[b, sl].cpu().numpy(), sep.cpu().numpy().astype(np.float64),
+                          f"grouped vs plain, batch {b} heads {begin}..{begin + count - 1}")
+
+
+def test_config5_grouped_deterministic():
+    """Ten grouped calls at the wide-state size, out cleared to NaN before each: identical bits."""
+    import torch
+
+    case = qi.CASES[5]
+    H_kv, M, S0_kv = qi.case_arrays(5)
+    H, S0 = _grouped_inputs(H_kv, S0_kv, case)
+    Hd, Md, Sd, first = _run_grouped(H, M, S0, case)
+    first = first.clone()
+    import linear_attention_context_amd as qla
+    out = torch.empty_like(first)
+    for i in range(10):
+        out.fill_(float("nan"))
+        qla.qla_correct_h0_grouped(Hd, Md, Sd, out, case.group_heads(), case.batch, case.heads, case.n_seg,
+                                   case.K, case.V)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), first.view(torch.int32)), f"call {i} differs"
 
 
 def test_config5_sentinels():
