@@ -59,8 +59,25 @@ def parse_args(argv=None):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source's code: // and /* */ comments and
+    blank lines removed, so that a comment edit does not invalidate counters
+    measured on unchanged code."""
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode("utf-8")).hexdigest()[:16]
+
+
+def kernel_name(variant: str, K: int) -> str:
+    """Device kernel that runs a variant ("kv_fwd", ...): forward at K <= 128 has
+    its own kernel (producer waves stage M), the rest share the general one."""
+    layout, direction = variant.split("_")
+    lay = 0 if layout == "kv" else 1
+    if direction == "fwd" and K <= 128:
+        return f"correct_h0_fwd_dma_kernel<{K}, {lay}>"
+    return f"correct_h0_kernel<{K}, {lay}, {0 if direction == 'fwd' else 1}>"
 
 
 def read_traffic():
@@ -69,8 +86,8 @@ def read_traffic():
     if not os.path.exists(TRAFFIC_FILE):
         return None
     text = open(TRAFFIC_FILE).read()
-    m_hash = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
-    m_bytes = re.search(r"HBM bytes per launch \(scaled\):\s*`?([0-9.eE+]+)", text)
+    m_hash = re.search(r"kernel source sha256\[:16\][^`]*`([0-9a-f]{16})`", text, re.I)
+    m_bytes = re.search(r"HBM bytes per launch \(scaled\):\s*`?([0-9.eE+]+)", text, re.I)
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_bytes.group(1))
@@ -223,7 +240,7 @@ def main(argv=None):
                    "timing": timing},
         "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_FP32_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_FP32_MFMA_TFLOPS,
-                     "traffic": read_traffic(), "kernel": f"correct_h0_kernel<128,{dominant}>",
+                     "traffic": read_traffic(), "kernel": kernel_name(dominant, K),
                      "flop_per_launch": flop_per_launch, "algorithmic_bytes_per_launch": bytes_per_launch,
                      "hbm_gbps": hbm_gbps, "hbm_frac": hbm_gbps / PEAK_HBM_GBPS,
                      "roofline_frac_of_max_bound": t_roof / t_dom},

@@ -13,36 +13,37 @@
 // Work decomposition.  Each column of the kv view evolves on its own
 // (p <- M_j p + h_j), so one workgroup carries one chain's recurrence for a
 // 16-column tile of the state, serially over the segments, and the chains x
-// tiles fill the GPU.  The workgroup's four waves split the K output rows: wave
-// w computes rows [w*K/4, (w+1)*K/4).  A wave therefore needs only its own
-// quarter of every M_j (its rows forward, its columns backward) and of every
-// H_j, and nothing it loads from HBM is shared with another wave: those
-// operands go straight from global memory into the wave's registers, one
-// panel ahead of use (a panel is a 64 KiB slice of M for the workgroup), in a
-// two-slot register ring.  The pages' Hopper kernel staged H and M through
-// shared-memory slots filled by a separate producer; here the prefetch target
-// is private to the consuming wave, so the slot-reuse race the note diagnoses
-// (section "决定性证据：错误值来自同一槽位的下一代": a slot read after it was
-// refilled with the segment two steps away) has no shared slot to happen in.
+// tiles fill the GPU.  The workgroup's MFMA waves split the K output rows:
+// wave w computes rows [w*K/W, (w+1)*K/W).
 //
-// The one shared buffer is the state exchange (the note's hd_shared role): each
-// step every wave needs all K rows of the previous state for its MFMA operand.
-// It lives in LDS as two slots.  Step s reads slot s&1 and writes slot (s+1)&1,
-// then every wave waits for its own LDS traffic (lgkmcnt(0)) and meets the
-// others at one s_barrier.  The slot written at step s was last read at step
-// s-1; every wave finished those reads before it arrived at the barrier that
-// closes step s-1, and no wave writes before passing that barrier.  The reads
-// of step s+1 come after the barrier that closes step s, which no wave reaches
-// before its writes landed.  Read-before-reuse holds by construction.
+// The shared state (the note's hd_shared role): each step every wave needs
+// all K rows of the previous state as its MFMA operand.  A wave's own rows it
+// keeps in registers (its accumulator is laid out as the operand it feeds);
+// the others come from LDS, which holds the state in two slots.  Step s opens
+// with one barrier (each wave first waits for its own LDS traffic), reads the
+// other waves' rows from slot s&1, and ends by writing its rows of the new
+// state to slot (s+1)&1.  That slot was last read during step s-1, and every
+// wave finished those reads before any wave passed the barrier that opens
+// step s; the reads of step s+1 come after the barrier that opens it, which
+// no wave reaches before its writes landed.  Read-before-reuse holds by
+// construction.
+//
+// Staging of M.  Forward at K <= 128 (FwdDma), dedicated producer waves copy
+// each M_j into one of two LDS stages, released by that same per-step barrier
+// (the pages' Hopper kernel also had a producer, with its own two-slot
+// buffers and hand-off; the slot-reuse race the note diagnoses, section
+// "决定性证据：错误值来自同一槽位的下一代", a slot read after it was refilled with
+// the segment two steps away, cannot happen here because a stage is refilled
+// only after the barrier that every reader of its previous contents has
+// passed).  Elsewhere (Tile) each wave prefetches exactly the share of M it
+// consumes into a private register ring, forward through a private LDS slot.
 //
 // Matrix cores: v_mfma_f32_16x16x4_f32 (fp32 in, fp32 accumulate).  Lane l =
-// 16*g + c feeds operand value (row c, k = 4g + q) on the q-th of four
-// instructions; the contraction order inside a 16-wide k block is thereby
-// {4g+q}, fixed, so results are bit-reproducible.  The accumulator fragment
-// (lane l, register r) is element (4g + r, c) of the 16x16 tile.  For kv the
-// tile computed is Y^T (rows = state columns v), for vk it is Y (rows = state
-// rows a): in both cases a lane's four registers are four consecutive floats
-// of the stored matrix, so H loads and out stores are 128-bit.
+// 16*g + c feeds A(row c, k) and B(k, column c) with k = 4g + q on the q-th of
+// four instructions; the contraction order inside a 16-wide k block is
+// thereby fixed, so results are bit-reproducible.  The accumulator (lane l,
+// register r) is element (4g + r, c) of the 16x16 tile Y = op(M) P: rows are
+// state rows, columns the tile's state columns.
 #include <hip/hip_runtime.h>
 
 #include "qla_internal.h"
@@ -67,8 +68,14 @@ typedef unsigned u2 __attribute__((ext_vector_type(2)));
 #ifndef QLA_STORE_AUX
 #define QLA_STORE_AUX 2  // non-temporal: out is not re-read
 #endif
-#ifndef QLA_BARRIER_FIRST
-#define QLA_BARRIER_FIRST 0
+#ifndef QLA_FWD_DMA
+#define QLA_FWD_DMA 1
+#endif
+#ifndef QLA_DMA_WAVES
+#define QLA_DMA_WAVES 4
+#endif
+#ifndef QLA_MO_AHEAD
+#define QLA_MO_AHEAD 2
 #endif
 constexpr int kTileV = 16;  // kv-view columns per workgroup
 
@@ -147,12 +154,15 @@ __device__ __forceinline__ float bload1(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, AUX));
 }
+__device__ __forceinline__ void bstore1(__amdgpu_buffer_rsrc_t r, unsigned off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, QLA_STORE_AUX);
+}
 __device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, unsigned off, f4 v)
 {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, (int)off, 0, QLA_STORE_AUX);
 }
 __device__ __forceinline__ void st4(float* p, f4 v) { *reinterpret_cast<f4*>(p) = v; }
-__device__ __forceinline__ void st2(float* p, f2 v) { *reinterpret_cast<f2*>(p) = v; }
 
 // Optional forced-delay schedule (built only into the race-test library): one
 // wave per step sleeps before reading the shared state slot, another before
@@ -177,17 +187,20 @@ struct Tile {
     static constexpr int T = S::T, KP = S::KP, NP = S::NP, BP = S::BP, LS = S::LS;
     static constexpr bool KV = LAYOUT == QLA_LAYOUT_KV;
     static constexpr bool FWD = DIR == QLA_DIR_FWD;
+    static constexpr bool STAGE = FWD;  // forward M goes through LDS staging
     static constexpr unsigned kMatBytes = (unsigned)K * K * 4u;
     // LDS: two state slots, plus one M staging slot per wave when forward.
     static constexpr int SS = S::SS;
     static constexpr int SF = S::STAGE_FLOATS;
-    static constexpr int LDS_FLOATS = S::STATE_FLOATS + (FWD ? S::WAVES * SS * SF : 0);
+    static constexpr int LDS_FLOATS = S::STATE_FLOATS + (STAGE ? S::WAVES * SS * SF : 0);
 
     // Per-lane constants of one workgroup.
     struct Lane {
         int wave, g, c, a0;
-        unsigned hoff[T];  // byte offsets of the lane's H/out vectors (kOutOfRange if masked)
+        unsigned hoff[T];  // vk: byte offsets of the lane's 16-byte H/out vectors
+        unsigned hk[T][4]; // kv: byte offset of fragment element (t, r)  (kOutOfRange if masked)
         unsigned moff;     // byte offset of the lane's first M operand (backward)
+        unsigned mown;     // same, for the own-row blocks in their register order (backward)
         unsigned mcoal;    // byte offset of the lane's first coalesced M chunk (forward)
         int prot, brot;    // k-order rotation of this wave: panels, then 16-k blocks in a panel
         unsigned state_bytes;
@@ -201,10 +214,15 @@ struct Tile {
         return FWD ? a0 + 16 * t + i : a0 + T * i + t;
     }
 
-    // Fragment element (t, r) of the state <-> component of the lane's
-    // 16-byte H/out vectors.  kv and vk-forward: vector t, component r.
-    // vk-backward: the lane's 4T values are contiguous, element (t, r) at
-    // flat index T*r + t.
+    // The accumulator computes Y (rows = state rows a) in every variant:
+    // fragment element (t, r) of lane (g, c) is row a = arow(t, 4g + r),
+    // column v = v0 + c.  That is also the layout the next step's MFMA
+    // operand needs for those rows, so a wave's own rows go from one step to
+    // the next in registers.
+    // vk memory is [v][a]: a lane's 4 (forward) or 4T (backward) rows are
+    // contiguous, read as 16-byte vectors; vector/component of element (t, r):
+    // forward vector t, component r; backward flat index T*r + t.  kv memory
+    // is [a][v]: one float per element, 16 lanes covering 64 contiguous bytes.
     static constexpr int vec_of(int t, int r) { return (KV || FWD) ? t : (T * r + t) >> 2; }
     static constexpr int comp_of(int t, int r) { return (KV || FWD) ? r : (T * r + t) & 3; }
 
@@ -217,17 +235,19 @@ struct Tile {
         L.c = lane & 15;
         L.a0 = L.wave * S::ROWS;
         L.state_bytes = (unsigned)K * V * 4u;
-        const bool valid = KV ? (v0 + 4 * L.g < V) : (v0 + L.c < V);
+        const bool valid = v0 + L.c < V;
 #pragma unroll
         for (int i = 0; i < T; ++i) {
-            int e;
-            if (KV) e = arow(L.a0, i, L.c) * V + v0 + 4 * L.g;
-            else if (FWD) e = (v0 + L.c) * K + L.a0 + 16 * i + 4 * L.g;
-            else e = (v0 + L.c) * K + L.a0 + 4 * T * L.g + 4 * i;
+            const int e = FWD ? (v0 + L.c) * K + L.a0 + 16 * i + 4 * L.g : (v0 + L.c) * K + L.a0 + 4 * T * L.g + 4 * i;
             L.hoff[i] = valid ? 4u * (unsigned)e : kOutOfRange;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                L.hk[i][r] = valid ? 4u * (unsigned)(arow(L.a0, i, 4 * L.g + r) * V + v0 + L.c) : kOutOfRange;
         }
         // Forward: M[a0 + c][4g]; backward: M[4g][a0 + T*c] (panel/block/tile offsets added per load).
         L.moff = 4u * (unsigned)(4 * L.g * K + L.a0 + T * L.c);
+        // Backward own-row block t, instruction q: k = a0 + T*(4g + q) + t.
+        L.mown = 4u * (unsigned)((L.a0 + 4 * T * L.g) * K + L.a0 + T * L.c);
         // Each wave walks the k range starting at its own rows (k = a0 ...):
         // the state of those rows is its own output, readable before the
         // other waves have written theirs.
@@ -237,10 +257,42 @@ struct Tile {
         return L;
     }
 
+    // Loads of one state matrix's share: T vectors (vk) or 4T floats (kv).
+    static constexpr int kStateLoads = KV ? 4 * T : T;
+
+    template <int I>
+    static __device__ __forceinline__ void load_state_one(f4 (&h)[T], __amdgpu_buffer_rsrc_t r, const Lane& L)
+    {
+        if constexpr (KV) h[I / 4][I % 4] = bload1<QLA_HLOAD_AUX>(r, L.hk[I / 4][I % 4]);
+        else h[I] = bload4<QLA_HLOAD_AUX>(r, L.hoff[I]);
+    }
+
     static __device__ __forceinline__ void load_state(f4 (&h)[T], __amdgpu_buffer_rsrc_t r, const Lane& L)
     {
+        if constexpr (KV) {
 #pragma unroll
-        for (int i = 0; i < T; ++i) h[i] = bload4(r, L.hoff[i]);
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) h[t][q] = bload1(r, L.hk[t][q]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < T; ++i) h[i] = bload4(r, L.hoff[i]);
+        }
+    }
+
+    static __device__ __forceinline__ void store_state(__amdgpu_buffer_rsrc_t r, const f4 (&x)[T], const Lane& L)
+    {
+        if constexpr (KV) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) bstore1(r, L.hk[t][q], x[t][q]);
+        } else {
+            f4 ov[T];
+            vecs_from_frag(ov, x);
+#pragma unroll
+            for (int i = 0; i < T; ++i) bstore4(r, L.hoff[i], ov[i]);
+        }
     }
 
     // Forward M staging.  Each wave owns a private LDS slot of ROWS x KP
@@ -264,47 +316,25 @@ struct Tile {
         return panel_of(p, L) * BP + ((b + L.brot) & (BP - 1));
     }
 
-    // Write the lane's fragment of the state into one LDS slot ([v][k] order).
+    // Write the lane's fragment of the state into one LDS slot ([v][k] order):
+    // element (t, r) is column v = c, row a = arow(t, 4g + r).
     static __device__ __forceinline__ void put_state(float* buf, const f4 (&x)[T], const Lane& L)
     {
         const int g = L.g, c = L.c, a0 = L.a0;
-        if (KV) {
-            // element (t, r): column v = 4g + r, row a = arow(t, c)
-            if (FWD) {
+        if (FWD) {
 #pragma unroll
-                for (int t = 0; t < T; ++t)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) buf[(4 * g + r) * LS + a0 + 16 * t + c] = x[t][r];
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float* dst = buf + (4 * g + r) * LS + a0 + T * c;
-                    if (T == 1) {
-                        dst[0] = x[0][r];
-                    } else if (T == 2) {
-                        st2(dst, f2{x[0][r], x[T - 1][r]});
-                    } else {
-                        st4(dst, f4{x[0][r], x[1 % T][r], x[2 % T][r], x[3 % T][r]});
-                    }
-                }
-            }
+            for (int t = 0; t < T; ++t) st4(buf + c * LS + a0 + 16 * t + 4 * g, x[t]);
         } else {
-            // element (t, r): column v = c, row a = arow(t, 4g + r)
-            if (FWD) {
+            // rows a0 + 4Tg + (T r + t): the lane's 4T values are contiguous
 #pragma unroll
-                for (int t = 0; t < T; ++t) st4(buf + c * LS + a0 + 16 * t + 4 * g, x[t]);
-            } else {
-                // rows a0 + 4Tg + (T r + t): the lane's 4T values are contiguous
+            for (int i = 0; i < T; ++i) {
+                f4 v;
 #pragma unroll
-                for (int i = 0; i < T; ++i) {
-                    f4 v;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int f = 4 * i + e;  // flat index = T*r + t
-                        v[e] = x[f % T][f / T];
-                    }
-                    st4(buf + c * LS + a0 + 4 * T * g + 4 * i, v);
+                for (int e = 0; e < 4; ++e) {
+                    const int f = 4 * i + e;  // flat index = T*r + t
+                    v[e] = x[f % T][f / T];
                 }
+                st4(buf + c * LS + a0 + 4 * T * g + 4 * i, v);
             }
         }
     }
@@ -347,7 +377,21 @@ struct Tile {
     static constexpr int F0 = R / gcd(R, NP);
     static constexpr int F = F0 * RH / gcd(F0, RH);
     static_assert(F >= 1 && F <= 6, "unroll block must be 1..6 steps");
-    static_assert(!(FWD && SS == 2) || D >= 2, "two-slot staging stages a unit loaded two units ahead");
+    static_assert(!(STAGE && SS == 2) || D >= 2, "two-slot staging stages a unit loaded two units ahead");
+
+    // Blocks of a step, in the wave's k order: the first T blocks of panel 0
+    // are the wave's own rows.  Their state operand is the wave's own output
+    // of the previous step, still in registers: own block t is accumulator
+    // tile t, so its k order follows the accumulator layout (forward the
+    // natural one; backward k = a0 + T*(4g + q) + t, and the M operand of
+    // those blocks is loaded in the same order).  Those MFMAs run while the
+    // other waves' rows are still being read from LDS.
+    static constexpr int kOwn = T;  // 16-k blocks of own rows
+    static_assert(kOwn <= BP, "own rows fit in the first panel");
+    // Forward, one panel per step, two staging slots: the first two staged
+    // M operand blocks of a step are read at the end of the previous step.
+    static constexpr bool kMoCarried = STAGE && SS == 2 && NP == 1;
+    static constexpr int MA = QLA_MO_AHEAD < BP ? QLA_MO_AHEAD : BP;  // staged reads run MA blocks ahead
 
     // ---- one load / staging-write instruction at a time -------------------
     // Loads of one M panel (this wave's share): forward, T*BP whole-line
@@ -355,16 +399,19 @@ struct Tile {
     // share); backward, 4*BP T-wide instructions (one per (b, q)).
     static constexpr int kPanelLoads = FWD ? T * BP : 4 * BP;
 
-    template <int I>
-    static __device__ __forceinline__ void load_m(f4 (&m)[T][BP], __amdgpu_buffer_rsrc_t Mr, int panel, const Lane& L)
+    template <int I, int TP>
+    static __device__ __forceinline__ void load_m(f4 (&m)[T][BP], __amdgpu_buffer_rsrc_t Mr, const Lane& L)
     {
-        const int pa = panel_of(panel, L);
-        if constexpr (FWD) {
+        const int pa = panel_of(TP, L);
+        if constexpr (STAGE) {
             m[I / BP][I % BP] = bload4<QLA_MLOAD_AUX>(Mr, L.mcoal + 4u * (unsigned)(I * S::RPI * K + pa * KP));
         } else {
-            // operand (a, k) = M[k][a], a = a0 + T*c + t, k = 16*kblock + 4g + q
+            // operand (a, k) = M[k][a], a = a0 + T*c + t; k = 16*kblock + 4g + q,
+            // or the own-row order for the first kOwn blocks of panel 0
             constexpr int b = I / 4, q = I % 4;
-            const unsigned off = L.moff + 4u * (unsigned)((pa * KP + 16 * ((b + L.brot) & (BP - 1)) + q) * K);
+            const unsigned off = (TP == 0 && b < kOwn)
+                                     ? L.mown + 4u * (unsigned)((T * q + b) * K)
+                                     : L.moff + 4u * (unsigned)((pa * KP + 16 * ((b + L.brot) & (BP - 1)) + q) * K);
             if constexpr (T == 1) {
                 m[0][b][q] = bload1<QLA_MLOAD_AUX>(Mr, off);
             } else if constexpr (T == 2) {
@@ -391,7 +438,6 @@ struct Tile {
     // Prefetch target of one panel: the unit D ahead.
     struct Prefetch {
         __amdgpu_buffer_rsrc_t Mr, Hr;
-        int panel;
     };
 
     // Issue prefetch loads [LO, HI) of the target unit: M instructions first,
@@ -402,9 +448,9 @@ struct Tile {
     {
         if constexpr (LO < HI) {
             if constexpr (LO < kPanelLoads)
-                load_m<LO>(m[(TLS * NP + TP) % R], pf.Mr, pf.panel, L);
+                load_m<LO, TP>(m[(TLS * NP + TP) % R], pf.Mr, L);
             else
-                h[TLS % RH][LO - kPanelLoads] = bload4<QLA_HLOAD_AUX>(pf.Hr, L.hoff[LO - kPanelLoads]);
+                load_state_one<LO - kPanelLoads>(h[TLS % RH], pf.Hr, L);
             issue_loads<LO + 1, HI, TLS, TP>(pf, m, h, L);
         }
     }
@@ -428,22 +474,27 @@ struct Tile {
         }
     }
 
-    // Working set of one step.
+    // Working registers, carried from step to step.
     struct StepCtx {
         f4 acc[T];
-        f4 pv[K / 16];
-        f4 mo[3][T];  // forward: staged M operand, read two blocks ahead
+        f4 own[T];     // the wave's own rows of the current state (operand of the own blocks)
+        f4 pv[K / 16]; // state operand blocks read from LDS
+        f4 mo[MA + 1][T];  // forward: staged M operand, read MA blocks ahead
+        f4 mh[MA][T];      // forward: the next panel's first MA blocks of it
         const float* cur;
         const float* st_cur;
         float* st_next;
+        __amdgpu_buffer_rsrc_t out_prev;  // out_j of the previous step (empty at step 0)
     };
 
-    // Blocks of a step, in the wave's k order: the first T blocks are the
-    // wave's own rows, whose state the wave wrote itself; the barrier that
-    // publishes the other waves' rows sits after the first of them, so its
-    // wait and the following state reads overlap the remaining own-row MFMAs.
-    static constexpr int kOwn = T;  // 16-k blocks of own rows
-    static constexpr int kOwnP0 = kOwn < BP ? kOwn : BP;
+    // The staged M operand of a panel's first MA blocks.
+    static __device__ __forceinline__ void read_mo_head(f4 (&mh)[MA][T], const float* st, const Lane& L)
+    {
+#pragma unroll
+        for (int b = 0; b < MA; ++b)
+#pragma unroll
+            for (int t = 0; t < T; ++t) mh[b][t] = stage_read(st, t, b, L);
+    }
 
     // One 16-k block B of panel P (local step LSX): half the block's MFMAs,
     // staged reads two blocks ahead, this block's share of the prefetch loads
@@ -456,46 +507,44 @@ struct Tile {
     {
         constexpr int slot = (LSX * NP + P) % R;
         constexpr int TLS = LSX + (P + D) / NP, TP = (P + D) % NP;
-        constexpr int NL = kPanelLoads + (TP == 0 ? T : 0);
+        constexpr int NL = kPanelLoads + (TP == 0 ? kStateLoads : 0);
         constexpr int l0 = NL * B / BP, l1 = NL * (B + 1) / BP;
-        constexpr int NW = (FWD && SS == 2) ? T * BP : 0;
-        constexpr int w0 = NW * B / BP, w1 = NW * (B + 1) / BP;
-        constexpr int nr = (FWD && B + 2 < BP) ? T : 0;
+        // Staging writes of the next unit go out over the first WB blocks, so
+        // that the LDS queue has drained them well before the step's end.
+        constexpr int NW = (STAGE && SS == 2) ? T * BP : 0;
+        constexpr int WB = BP > 2 ? BP - 2 : BP;
+        constexpr int w0 = B < WB ? NW * B / WB : NW, w1 = B < WB ? NW * (B + 1) / WB : NW;
+        constexpr int nr = (STAGE && B + MA < BP) ? T : 0;
+        // After the last staging write: the next step's first staged operand
+        // blocks, early enough to stay off the step's closing LDS wait.
+        constexpr int nmo = (kMoCarried && P == NP - 1 && B == (WB < BP ? WB : BP - 1)) ? MA * T : 0;
 
         auto mfma = [&](int q) {
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                const float pk = X.pv[P * BP + B][q];
-                const float mk = FWD ? X.mo[B % 3][t][q] : m[slot][t][B][q];
-                if (KV)
-                    X.acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(pk, mk, X.acc[t], 0, 0, 0);
-                else
-                    X.acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(mk, pk, X.acc[t], 0, 0, 0);
+                const float pk = (P == 0 && B < kOwn) ? X.own[B][q] : X.pv[P * BP + B][q];
+                const float mk = STAGE ? X.mo[B % (MA + 1)][t][q] : m[slot][t][B][q];
+                X.acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(mk, pk, X.acc[t], 0, 0, 0);
             }
         };
         mfma(0);
         mfma(1);
         if constexpr (nr > 0) {
 #pragma unroll
-            for (int t = 0; t < T; ++t) X.mo[(B + 2) % 3][t] = stage_read(X.st_cur, t, B + 2, L);
+            for (int t = 0; t < T; ++t) X.mo[(B + MA) % (MA + 1)][t] = stage_read(X.st_cur, t, B + MA, L);
         }
         issue_loads<l0, l1, TLS, TP>(pf, m, h, L);
         if constexpr (NW > 0) issue_writes<w0, w1>(X.st_next, m[(LSX * NP + P + 1) % R]);
         mfma(2);
         mfma(3);
+        if constexpr (nmo > 0) read_mo_head(X.mh, X.st_next, L);
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * T, 0);                                // MFMA
         if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);             // DS read
         if constexpr (l1 > l0) __builtin_amdgcn_sched_group_barrier(0x020, l1 - l0, 0);       // VMEM read
         if constexpr (w1 > w0) __builtin_amdgcn_sched_group_barrier(0x200, w1 - w0, 0);       // DS write
+        if constexpr (nmo > 0) __builtin_amdgcn_sched_group_barrier(0x100, nmo, 0);           // DS read
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * T, 0);                                // MFMA
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (P == 0 && B == 0 && !QLA_BARRIER_FIRST) {
-            // Publish / acquire the state rows of the other waves, then read
-            // their part of this panel's state operand.
-            lds_handoff();
-            read_pv<0, kOwnP0, BP>(X.pv, X.cur, L);
-            __builtin_amdgcn_sched_barrier(0);
-        }
         if constexpr (B + 1 < BP) block<LSX, P, B + 1>(X, pf, m, h, L);
     }
 
@@ -510,7 +559,7 @@ struct Tile {
         const bool live = ts < C.n_seg;
         const int tj = live ? seg(C, ts) : 0;
         const Prefetch pf{rsrc(C.M + (size_t)tj * K * K, live ? kMatBytes : 0u),
-                          rsrc(C.H + (size_t)tj * (L.state_bytes / 4), live ? L.state_bytes : 0u), (P + D) % NP};
+                          rsrc(C.H + (size_t)tj * (L.state_bytes / 4), live ? L.state_bytes : 0u)};
         // Forward: this panel's M is read from staging slot (unit & 1),
         // written during the previous panel (two slots) or just below (one).
         // The next panel goes into the other slot, which the previous panel
@@ -520,22 +569,18 @@ struct Tile {
         X.st_cur = stage + (SS == 2 ? (unit & 1) * SF : 0);
         X.st_next = stage + (SS == 2 ? ((unit + 1) & 1) * SF : 0);
 
-        // State operand: panel 0's own-row blocks (own writes, no barrier
-        // needed); later panels after the barrier, in full.
-        if constexpr (P == 0) read_pv<0, 0, kOwnP0>(X.pv, X.cur, L);
-        else read_pv<P, 0, BP>(X.pv, X.cur, L);
-        if constexpr (FWD && SS == 1) issue_writes<0, T * BP>(stage, m[slot]);
-        if constexpr (FWD) {
+        // State operand from LDS: all blocks but panel 0's own rows.
+        read_pv<P, (P == 0 ? kOwn : 0), BP>(X.pv, X.cur, L);
+        // The previous step's out_j leaves after the barrier, off the path
+        // that leads to it.
+        if constexpr (P == 0) store_state(X.out_prev, X.own, L);
+        if constexpr (STAGE && SS == 1) issue_writes<0, T * BP>(stage, m[slot]);
+        if constexpr (STAGE && !(P == 0 && kMoCarried)) read_mo_head(X.mh, X.st_cur, L);
+        if constexpr (STAGE) {
 #pragma unroll
-            for (int t = 0; t < T; ++t) X.mo[0][t] = stage_read(X.st_cur, t, 0, L);
-            if constexpr (BP > 1) {
+            for (int b = 0; b < MA; ++b)
 #pragma unroll
-                for (int t = 0; t < T; ++t) X.mo[1][t] = stage_read(X.st_cur, t, 1, L);
-            }
-        }
-        if constexpr (P == 0 && QLA_BARRIER_FIRST) {
-            lds_handoff();
-            read_pv<0, kOwnP0, BP>(X.pv, X.cur, L);
+                for (int t = 0; t < T; ++t) X.mo[b][t] = X.mh[b][t];
         }
         __builtin_amdgcn_sched_barrier(0);
         block<LSX, P, 0>(X, pf, m, h, L);
@@ -543,68 +588,71 @@ struct Tile {
     }
 
     // One segment step with compile-time local index LSX (position in the
-    // unrolled block).  Reads LDS state slot s & 1, writes slot (s + 1) & 1.
-    // Slot (s+1)&1 was last read during step s-1; every wave finished those
-    // reads before arriving at the barrier inside step s, and the writes come
-    // after it.  The other waves' rows of slot s&1 are read after that same
-    // barrier, which no wave reaches before its step s-1 writes landed.
+    // unrolled block).  The step opens with the barrier that publishes the
+    // state rows every wave wrote to LDS slot s & 1 at the end of step s-1
+    // (each wave first waits for its own LDS traffic), then reads the other
+    // waves' rows from that slot; its own rows it already holds, and it
+    // stores them as out of step s-1.  It ends by writing its rows of the new
+    // state to slot (s + 1) & 1.  That slot was last read during step s-1,
+    // and every wave finished those reads (the wait before the barrier)
+    // before any wave passed the barrier that opens step s.
     template <int LSX>
-    static __device__ __forceinline__ void step(int s, const Chain& C, f4 (&m)[R][T][BP], f4 (&h)[RH][T],
-                                                float* lds, const Lane& L)
+    static __device__ __forceinline__ void step(int s, StepCtx& X, const Chain& C, f4 (&m)[R][T][BP],
+                                                f4 (&h)[RH][T], float* lds, const Lane& L)
     {
-        const int j = seg(C, s);
+        s = __builtin_amdgcn_readfirstlane(s);  // uniform: keeps the step's descriptors scalar
         float* nxt = lds + ((s + 1) & 1) * (kTileV * LS);
         float* stage = lds + S::STATE_FLOATS + L.wave * SS * SF;
+        const int jp = s > 0 ? seg(C, s - 1) : 0;
+        X.out_prev = rsrc(C.out + (size_t)jp * (L.state_bytes / 4), s > 0 ? L.state_bytes : 0u);
 
         __builtin_amdgcn_sched_barrier(0);
+        lds_handoff();
         debug_delay(L.wave, s, 0);
-        StepCtx X;
         X.cur = lds + (s & 1) * (kTileV * LS);
 #pragma unroll
         for (int t = 0; t < T; ++t) X.acc[t] = f4{0.f, 0.f, 0.f, 0.f};
         panel<LSX, 0>(s, X, C, m, h, stage, L);
 
-        // Correct: P = Y + X(H_j); emit out_j; hand the state to the next step.
+        // Correct: P = Y + X(H_j); hand the state to the next step (LDS for
+        // the other waves, registers for this one, which also emits it).
         f4 hx[T];
         frag_from_vecs(hx, h[LSX % RH]);
 #pragma unroll
         for (int t = 0; t < T; ++t) X.acc[t] += hx[t];
-        f4 ov[T];
-        vecs_from_frag(ov, X.acc);
-        const __amdgpu_buffer_rsrc_t Or = rsrc(C.out + (size_t)j * (L.state_bytes / 4), L.state_bytes);
-#pragma unroll
-        for (int i = 0; i < T; ++i) bstore4(Or, L.hoff[i], ov[i]);
         debug_delay(L.wave, s, 1);
         put_state(nxt, X.acc, L);
+#pragma unroll
+        for (int t = 0; t < T; ++t) X.own[t] = X.acc[t];
         __builtin_amdgcn_sched_barrier(0);
     }
 
     // Remaining steps after the unrolled loop (fewer than F), straight-line.
     template <int LSX>
-    static __device__ __forceinline__ void tail(int s, int rem, const Chain& C, f4 (&m)[R][T][BP],
+    static __device__ __forceinline__ void tail(int s, int rem, StepCtx& X, const Chain& C, f4 (&m)[R][T][BP],
                                                 f4 (&h)[RH][T], float* lds, const Lane& L)
     {
         if constexpr (LSX < F - 1) {
             if (rem > LSX) {
-                step<LSX>(s + LSX, C, m, h, lds, L);
-                tail<LSX + 1>(s, rem, C, m, h, lds, L);
+                step<LSX>(s + LSX, X, C, m, h, lds, L);
+                tail<LSX + 1>(s, rem, X, C, m, h, lds, L);
             }
         }
     }
 
-    // Prologue loads: units 0 .. D-1 (and the H of the steps they start).
-    template <int V_>
+    // Prologue loads: units LO .. HI-1 (and the H of the steps they start).
+    template <int LO, int HI>
     static __device__ __forceinline__ void prologue(const Chain& C, f4 (&m)[R][T][BP], f4 (&h)[RH][T],
                                                     const Lane& L)
     {
-        if constexpr (V_ < D) {
-            constexpr int TLS = V_ / NP, TP = V_ % NP;
+        if constexpr (LO < HI) {
+            constexpr int TLS = LO / NP, TP = LO % NP;
             const bool live = TLS < C.n_seg;
             const int tj = live ? seg(C, TLS) : 0;
             const Prefetch pf{rsrc(C.M + (size_t)tj * K * K, live ? kMatBytes : 0u),
-                              rsrc(C.H + (size_t)tj * (L.state_bytes / 4), live ? L.state_bytes : 0u), TP};
-            issue_loads<0, kPanelLoads + (TP == 0 ? T : 0), TLS, TP>(pf, m, h, L);
-            prologue<V_ + 1>(C, m, h, L);
+                              rsrc(C.H + (size_t)tj * (L.state_bytes / 4), live ? L.state_bytes : 0u)};
+            issue_loads<0, kPanelLoads + (TP == 0 ? kStateLoads : 0), TLS, TP>(pf, m, h, L);
+            prologue<LO + 1, HI>(C, m, h, L);
         }
     }
 
@@ -618,27 +666,216 @@ struct Tile {
 
         f4 m[R][T][BP];
         f4 h[RH][T];
-        // Prologue: the first D units of M (and their steps' H), then the
-        // initial state into LDS slot 0.
-        prologue<0>(C, m, h, L);
-        if constexpr (FWD && SS == 2) issue_writes<0, T * BP>(lds + S::STATE_FLOATS + L.wave * SS * SF, m[0]);
-        {
-            f4 sv[T], sx[T];
-            load_state(sv, rsrc(S0 ? S0 + chain * state : H, S0 ? L.state_bytes : 0u), L);
-            frag_from_vecs(sx, sv);
-            put_state(lds, sx, L);
-        }
+        StepCtx X;
+        // Prologue.  A CU's vector memory path takes about 64 bytes per clock,
+        // and a wave stalls at a load it cannot queue, so the loads go out in
+        // the order they are needed: the initial state and the first unit of
+        // M (with H of step 0); that unit's staging and the initial state's
+        // hand-off; only then the rest of the prefetch distance, which the
+        // first steps' work covers.
+        f4 sv[T];
+        load_state(sv, rsrc(S0 ? S0 + chain * state : H, S0 ? L.state_bytes : 0u), L);
+        prologue<0, 1>(C, m, h, L);
+        frag_from_vecs(X.own, sv);
+        put_state(lds, X.own, L);
+        float* stage0 = lds + S::STATE_FLOATS + L.wave * SS * SF;
+        if constexpr (STAGE && SS == 2) issue_writes<0, T * BP>(stage0, m[0]);
+        if constexpr (kMoCarried) read_mo_head(X.mh, stage0, L);
+        prologue<1, D>(C, m, h, L);
 
         int s = 0;
         for (; s + F <= n_seg; s += F) {
-            step<0>(s, C, m, h, lds, L);
-            if constexpr (F > 1) step<1 % F>(s + 1, C, m, h, lds, L);
-            if constexpr (F > 2) step<2 % F>(s + 2, C, m, h, lds, L);
-            if constexpr (F > 3) step<3 % F>(s + 3, C, m, h, lds, L);
-            if constexpr (F > 4) step<4 % F>(s + 4, C, m, h, lds, L);
-            if constexpr (F > 5) step<5 % F>(s + 5, C, m, h, lds, L);
+            step<0>(s, X, C, m, h, lds, L);
+            if constexpr (F > 1) step<1 % F>(s + 1, X, C, m, h, lds, L);
+            if constexpr (F > 2) step<2 % F>(s + 2, X, C, m, h, lds, L);
+            if constexpr (F > 3) step<3 % F>(s + 3, X, C, m, h, lds, L);
+            if constexpr (F > 4) step<4 % F>(s + 4, X, C, m, h, lds, L);
+            if constexpr (F > 5) step<5 % F>(s + 5, X, C, m, h, lds, L);
         }
-        tail<0>(s, n_seg - s, C, m, h, lds, L);
+        tail<0>(s, n_seg - s, X, C, m, h, lds, L);
+        store_state(rsrc(C.out + (size_t)seg(C, n_seg - 1) * (L.state_bytes / 4), L.state_bytes), X.own, L);
+    }
+};
+
+// Forward, K <= 128: producer waves and MFMA waves.  Waves CW .. CW+PW-1 of
+// the workgroup only move M: together they copy each M_j whole from global
+// memory into one of two LDS stages with 16-byte LDS-DMA buffer loads (the
+// data never passes through registers; each producer issues an equal share
+// of the copies, so that enough of them are in flight to cover the memory
+// latency), wait for them, and join the step barrier.
+// Waves 0 .. CW-1 compute as above, reading their rows of M from the stage;
+// they issue no M loads, so their instruction streams are MFMAs and LDS
+// reads.  One barrier per step orders everything: after the barrier that
+// opens step s the producer refills the stage of unit s-1 with unit s+1
+// (every MFMA wave finished reading it before arriving), and unit s+1 has
+// landed before the producer arrives at the barrier that opens step s+1.
+// The stage holds M row-major with each row's 16-byte chunks XOR-swizzled
+// by the row's low four bits, so the whole-row copy and the MFMA-layout
+// reads are both free of bank conflicts.
+template <int K, int LAYOUT>
+struct FwdDma {
+    static constexpr int CW = QLA_WAVES(K, true);
+    static constexpr int PW = QLA_DMA_WAVES;           // producer waves
+    using Tl = Tile<K, LAYOUT, QLA_DIR_FWD, CW>;
+    using S = typename Tl::S;
+    using Lane = typename Tl::Lane;
+    using Chain = typename Tl::Chain;
+    static constexpr int T = S::T, BP = S::BP, LS = S::LS;
+    static_assert(S::NP == 1, "one panel per step");
+    static constexpr int kOwn = T;
+    static constexpr int MA = 2;                      // staged reads run two blocks ahead
+    static constexpr int STAGE = K * K;               // floats per M stage
+    static constexpr int LDS_FLOATS = S::STATE_FLOATS + 2 * STAGE;
+    static constexpr int kDma = K * K / 256;          // 1 KiB copies per M
+    static_assert(kDma % PW == 0, "equal producer shares");
+    static constexpr unsigned kMatBytes = (unsigned)K * K * 4u;
+
+    struct Ctx {
+        f4 acc[T];
+        f4 own[T];
+        f4 pv[K / 16];
+        f4 mo[MA + 1][T];
+        const float* cur;
+        const float* st;
+        __amdgpu_buffer_rsrc_t out_prev;
+    };
+
+    // ---- producer ---------------------------------------------------------
+    // Copy M_j into a stage: copy i fills stage floats [256 i, 256 i + 256);
+    // lane l's 16 bytes land at float 256 i + 4 l = (row, swizzled chunk).
+    // Producer p issues copies p, p + PW, p + 2 PW, ...
+    static __device__ __forceinline__ void dma_unit(const float* Mj, float* stage, int p)
+    {
+        const __amdgpu_buffer_rsrc_t r = rsrc(Mj, kMatBytes);
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int k = 0; k < kDma / PW; ++k) {
+            const int i = k * PW + p;
+            const int q = 256 * i + 4 * lane;
+            const int row = q / K, chunk = (q % K) / 4;
+            const int src = row * K + 4 * (chunk ^ (row & 15));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void*)(stage + 256 * i), 16, 4 * src, 0, 0, 0);
+        }
+    }
+
+    static __device__ __forceinline__ void producer(const Chain& C, float* lds, int p)
+    {
+        float* stages = lds + S::STATE_FLOATS;
+        dma_unit(C.M + (size_t)Tl::seg(C, 0) * K * K, stages, p);
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        for (int s = 0; s + 1 < C.n_seg; ++s) {
+            dma_unit(C.M + (size_t)Tl::seg(C, s + 1) * K * K, stages + ((s + 1) & 1) * STAGE, p);
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+    }
+
+    // ---- MFMA waves -------------------------------------------------------
+    template <int B>
+    static __device__ __forceinline__ void blocks(Ctx& X, const Lane& L)
+    {
+        constexpr int nr = B + MA < BP ? T : 0;
+        auto mfma = [&](int q) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const float pk = B < kOwn ? X.own[B][q] : X.pv[B][q];
+                X.acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(X.mo[B % (MA + 1)][t][q], pk, X.acc[t], 0, 0, 0);
+            }
+        };
+        mfma(0);
+        mfma(1);
+        if constexpr (nr > 0) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) X.mo[(B + MA) % (MA + 1)][t] = Tl::stage_read(X.st, t, B + MA, L);
+        }
+        mfma(2);
+        mfma(3);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * T, 0);
+        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * T, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (B + 1 < BP) blocks<B + 1>(X, L);
+    }
+
+    // Step s (LSX = s & 1 selects the H register slot).  Barrier; operand
+    // reads (first staged M blocks, the other waves' state rows); out of step
+    // s-1 and H of step s+1 on the way; the MFMAs; P = Y + X(H_j) into the
+    // next state slot and the own-row registers.
+    template <int LSX>
+    static __device__ __forceinline__ void step(int s, Ctx& X, const Chain& C, f4 (&h)[2][T], float* lds,
+                                                const Lane& L)
+    {
+        s = __builtin_amdgcn_readfirstlane(s);  // uniform: keeps the step's descriptors scalar
+        float* nxt = lds + ((s + 1) & 1) * (kTileV * LS);
+        const int jp = s > 0 ? Tl::seg(C, s - 1) : 0;
+        X.out_prev = rsrc(C.out + (size_t)jp * (L.state_bytes / 4), s > 0 ? L.state_bytes : 0u);
+        const bool live = s + 1 < C.n_seg;
+        const __amdgpu_buffer_rsrc_t Hr =
+            rsrc(C.H + (size_t)(live ? Tl::seg(C, s + 1) : 0) * (L.state_bytes / 4), live ? L.state_bytes : 0u);
+
+        __builtin_amdgcn_sched_barrier(0);
+        lds_handoff();
+        debug_delay(L.wave, s, 0);
+        X.cur = lds + (s & 1) * (kTileV * LS);
+        X.st = lds + S::STATE_FLOATS + (s & 1) * STAGE + L.a0 * K;
+#pragma unroll
+        for (int b = 0; b < MA; ++b)
+#pragma unroll
+            for (int t = 0; t < T; ++t) X.mo[b][t] = Tl::stage_read(X.st, t, b, L);
+        Tl::template read_pv<0, kOwn, BP>(X.pv, X.cur, L);
+#pragma unroll
+        for (int t = 0; t < T; ++t) X.acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+        __builtin_amdgcn_sched_barrier(0);
+        blocks<0>(X, L);
+        // The wave's few global accesses go out once the step's MFMAs are
+        // issued: right after the barrier the producers fill the CU's vector
+        // memory queue, and a load or store waiting for a slot there would
+        // hold up this wave's MFMAs.
+        Tl::store_state(X.out_prev, X.own, L);
+        Tl::load_state(h[(LSX + 1) & 1], Hr, L);
+
+        f4 hx[T];
+        Tl::frag_from_vecs(hx, h[LSX & 1]);
+#pragma unroll
+        for (int t = 0; t < T; ++t) X.acc[t] += hx[t];
+        debug_delay(L.wave, s, 1);
+        Tl::put_state(nxt, X.acc, L);
+#pragma unroll
+        for (int t = 0; t < T; ++t) X.own[t] = X.acc[t];
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    static __device__ __forceinline__ void consumer(const Chain& C, const float* S0, float* lds, size_t chain,
+                                                    int tile, int V)
+    {
+        const Lane L = Tl::make_lane(tile * kTileV, V);
+        const size_t state = (size_t)K * V;
+        Ctx X;
+        f4 h[2][T];
+        f4 sv[T];
+        Tl::load_state(sv, rsrc(S0 ? S0 + chain * state : C.H, S0 ? L.state_bytes : 0u), L);
+        Tl::load_state(h[0], rsrc(C.H + (size_t)Tl::seg(C, 0) * (L.state_bytes / 4), L.state_bytes), L);
+        Tl::frag_from_vecs(X.own, sv);
+        Tl::put_state(lds, X.own, L);
+        int s = 0;
+        for (; s + 2 <= C.n_seg; s += 2) {
+            step<0>(s, X, C, h, lds, L);
+            step<1>(s + 1, X, C, h, lds, L);
+        }
+        if (s < C.n_seg) step<0>(s, X, C, h, lds, L);
+        Tl::store_state(rsrc(C.out + (size_t)Tl::seg(C, C.n_seg - 1) * (L.state_bytes / 4), L.state_bytes), X.own,
+                        L);
+    }
+
+    static __device__ __forceinline__ void run(const float* H, const float* M, const float* S0, float* out,
+                                               int n_seg, int V, size_t chain, int tile, float* lds)
+    {
+        const size_t state = (size_t)K * V;
+        const Chain C{M + chain * (size_t)n_seg * K * K, H + chain * state * n_seg, out + chain * state * n_seg,
+                      n_seg};
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        if (wave >= CW) producer(C, lds, wave - CW);
+        else consumer(C, S0, lds, chain, tile, V);
     }
 };
 
@@ -670,6 +907,18 @@ __global__ __launch_bounds__(64 * QLA_WAVES(K, DIR == QLA_DIR_FWD)) void correct
     Tl::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds);
 }
 
+template <int K, int LAYOUT>
+__global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void correct_h0_fwd_dma_kernel(
+    const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles)
+{
+    using D = FwdDma<K, LAYOUT>;
+    __shared__ __attribute__((aligned(16))) float lds[D::LDS_FLOATS];
+    const int id = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int chain = id / tiles;
+    const int tile = id - chain * tiles;
+    D::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds);
+}
+
 template <int K>
 __global__ __launch_bounds__(64 * QLA_GROUPED_WAVES(K)) void correct_h0_grouped_kernel(
     const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles, int heads,
@@ -699,6 +948,11 @@ hipError_t launch_one(const LaunchArgs& a)
 {
     const int tiles = (a.V + kTileV - 1) / kTileV;
     const dim3 grid((unsigned)(a.chains * tiles));
+    if constexpr (QLA_FWD_DMA && DIR == QLA_DIR_FWD && K <= 128) {
+        hipLaunchKernelGGL((correct_h0_fwd_dma_kernel<K, LAYOUT>), grid, dim3(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)), 0,
+                           (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((correct_h0_kernel<K, LAYOUT, DIR>), grid, dim3(64 * Plain<K, LAYOUT, DIR>::WAVES), 0,
                        (hipStream_t)a.stream, a.H,
                        a.M, a.S0, a.out, a.n_seg, a.V, tiles);
