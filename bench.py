@@ -4,9 +4,12 @@ Workload (one "step"): the 32K-token x 32-head forward correction in both state
 layouts -- batch 1, 32 heads, 8 segments of 4096 tokens, K = V = 128, one
 qla_correct_h0 call for kv and one for vk (512 segment-state corrections).
 Inputs are seeded synthetic data (H ~ N(0,1), M = 0.9 I + N(0, 0.1/K), S0 ~
-N(0,1)), already resident in HBM when timing starts.  Each call in a step reads
-its own buffers, and steps rotate over enough buffer sets (> 256 MB MALL) that
-every call streams its inputs from HBM.
+N(0,1)), already resident in HBM when timing starts.
+
+Cache perturbation: each variant's calls cycle over --rotate (16) buffer sets
+of their own, 16 x 52.4 MB = 839 MB > the 256 MB MALL, so every call streams
+its inputs from HBM.  The same calls on one resident set (warm) and the
+bandwidth of a plain 1 GiB device copy are reported beside it.
 
 Timing: the steps' kv calls run back to back, then their vk calls, with HIP
 events on the launch stream at the boundaries (--mode direct, default).
@@ -16,7 +19,8 @@ captured in hipGraphs of 16 calls and replayed.
 Prints one JSON line.  value = corrections/s of the whole job; roofline =
 the dominant kernel's achieved TFLOP/s (its average launch duration from those
 events) against the fp32 matrix peak; cpu_baseline = the fp64 oracle on the
-host, one thread, on the same workload.
+host, one thread, on the same workload.  --sweep times the pages' sweep
+instead (one JSON line per point).
 """
 from __future__ import annotations
 
@@ -38,7 +42,7 @@ METRIC = "segment-state corrections/s + achieved HBM GB/s (% roofline), 32K tok 
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_context_amd", "csrc", "qla_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "correct_h0_kv_fwd_32k32h_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "correct_h0_fwd_32k32h_traffic.md")
 
 
 def parse_args(argv=None):
@@ -49,10 +53,14 @@ def parse_args(argv=None):
     p.add_argument("--mode", choices=("direct", "graph"), default="direct",
                    help="direct launches (default) or replays of captured hipGraphs")
     p.add_argument("--graph-calls", type=int, default=16, help="launches per captured graph (--mode graph)")
-    p.add_argument("--rotate", type=int, default=4, help="buffer sets cycled by the steps")
+    p.add_argument("--rotate", type=int, default=16,
+                   help="buffer sets cycled by each variant's calls (16 x 52.4 MB > the 256 MB MALL)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true", help="skip the oracle check of the timed outputs")
+    p.add_argument("--sweep", action="store_true",
+                   help="instead of the step: time the pages' sweep (4K/8K/32K tokens x 4/16/32 heads x "
+                        "{kv,vk} x {fwd,bwd} x S0 on/off), one JSON line per point")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for scaling rocprof byte counters)")
     return p.parse_args(argv)
@@ -80,17 +88,97 @@ def kernel_name(variant: str, K: int) -> str:
     return f"correct_h0_kernel<{K}, {lay}, {0 if direction == 'fwd' else 1}>"
 
 
-def read_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source."""
+def read_traffic(kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter
+    summary, if that summary was taken on the current kernel code."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     text = open(TRAFFIC_FILE).read()
     m_hash = re.search(r"kernel source sha256\[:16\][^`]*`([0-9a-f]{16})`", text, re.I)
-    m_bytes = re.search(r"HBM bytes per launch \(scaled\):\s*`?([0-9.eE+]+)", text, re.I)
+    m_bytes = re.search(r"HBM bytes per launch \(scaled\),\s*`" + re.escape(kernel) + r"`:\s*([0-9.eE+]+)", text,
+                        re.I)
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_bytes.group(1))
+
+
+def measured_copy_gbps(torch, dev) -> float:
+    """Read + write bytes per second of a plain 1 GiB device-to-device copy."""
+    n = 1 << 28
+    a = torch.ones(n, device=dev)
+    b = torch.empty(n, device=dev)
+    for _ in range(2):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * 4 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    return gbps
+
+
+def run_sweep(args) -> int:
+    """The pages' sweep at K = V = 128: per point and variant, the per-call time
+    on one resident buffer set (warm) and over rotating sets (> 512 MiB of
+    inputs where that takes at most 64 sets), one JSON line each."""
+    import torch
+
+    import linear_attention_context_amd as qla
+    import qla_inputs as qi
+
+    qla.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    K = V = 128
+    copy_gbps = measured_copy_gbps(torch, dev)
+    for tokens in qi.SWEEP_TOKENS:
+        for heads in qi.SWEEP_HEADS:
+            n = tokens // qi.SEG_TOKENS
+            H, M, S0 = qi.sweep_arrays(tokens, heads)
+            set_bytes = 4 * heads * (n * (2 * K * V + K * K) + K * V)
+            rot = max(1, min(64, -(-(512 << 20) // set_bytes)))
+            for layout in ("kv", "vk"):
+                Hl = H if layout == "kv" else qi.to_vk(H)
+                Sl = S0 if layout == "kv" else qi.to_vk(S0)
+                sets = [dict(H=torch.from_numpy(Hl).to(dev), M=torch.from_numpy(M).to(dev),
+                             S0=torch.from_numpy(Sl).to(dev), out=torch.empty(Hl.shape, device=dev))
+                        for _ in range(rot)]
+                for direction in ("fwd", "bwd"):
+                    for s0_on in (True, False):
+                        def call(x):
+                            qla.qla_correct_h0(x["H"], x["M"], x["S0"] if s0_on else None, x["out"], layout,
+                                               direction, 1, heads, n, K, V, stream=stream.cuda_stream)
+                        times = {}
+                        for label, order in (("warm", [0] * 64), ("rotated", [i % rot for i in range(max(64, rot))])):
+                            for i in order[:8]:
+                                call(sets[i])
+                            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                            e0.record(stream)
+                            for i in order:
+                                call(sets[i])
+                            e1.record(stream)
+                            torch.cuda.synchronize()
+                            times[label] = e0.elapsed_time(e1) * 1e3 / len(order)
+                        nbytes = 4.0 * heads * (n * (2 * K * V + K * K) + (K * V if s0_on else 0))
+                        flop = heads * n * 2.0 * K * K * V
+                        t = times["rotated"] * 1e-6
+                        t_roof = max(flop / (PEAK_FP32_MFMA_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9))
+                        print(json.dumps({
+                            "sweep": {"tokens": tokens, "heads": heads, "n_seg": n, "layout": layout,
+                                      "direction": direction, "s0": s0_on},
+                            "us_per_call": times["rotated"], "warm_us_per_call": times["warm"],
+                            "buffer_sets": rot,
+                            "corrections_per_s": heads * n / t,
+                            "tflops": flop / t / 1e12, "hbm_gbps": nbytes / t / 1e9,
+                            "roofline_frac": t_roof / t, "measured_copy_gbps": copy_gbps,
+                        }), flush=True)
+                del sets
+                torch.cuda.empty_cache()
+    return 0
 
 
 def main(argv=None):
@@ -99,6 +187,9 @@ def main(argv=None):
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on a "
               "single MI355X: chains shard across GPUs with no exchange, see DESIGN.md)", file=sys.stderr)
         return 2
+
+    if args.sweep:
+        return run_sweep(args)
 
     import torch
 
@@ -204,6 +295,22 @@ def main(argv=None):
         timing = "direct launches, each variant's K calls back to back between HIP events"
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
 
+    # Context: the same calls on one resident buffer set (inputs warm in
+    # L2/MALL), and the streaming bandwidth of a plain 1 GiB device copy.
+    warm_us = {}
+    for v, (layout, direction) in enumerate(variants):
+        nw = 64
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(4):
+            launch(sets[0][v], stream.cuda_stream)
+        e0.record(stream)
+        for _ in range(nw):
+            launch(sets[0][v], stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        warm_us[f"{layout}_{direction}"] = e0.elapsed_time(e1) * 1e3 / nw
+    copy_gbps = measured_copy_gbps(torch, dev)
+
     per_call_us = {}
     for v, (layout, direction) in enumerate(variants):
         d = per_launch[v]
@@ -240,11 +347,14 @@ def main(argv=None):
                    "timing": timing},
         "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_FP32_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_FP32_MFMA_TFLOPS,
-                     "traffic": read_traffic(), "kernel": kernel_name(dominant, K),
+                     "traffic": read_traffic(kernel_name(dominant, K)), "kernel": kernel_name(dominant, K),
                      "flop_per_launch": flop_per_launch, "algorithmic_bytes_per_launch": bytes_per_launch,
                      "hbm_gbps": hbm_gbps, "hbm_frac": hbm_gbps / PEAK_HBM_GBPS,
                      "roofline_frac_of_max_bound": t_roof / t_dom},
         "per_call_us": per_call_us,
+        "warm_single_buffer_us_per_call": warm_us,
+        "measured_copy_gbps": copy_gbps,
+        "hbm_frac_of_measured_copy": hbm_gbps / copy_gbps,
         "host_us_per_call": host_us,
         "kernel_source_sha256_16": kernel_source_hash(),
     }

@@ -65,14 +65,20 @@ typedef unsigned u2 __attribute__((ext_vector_type(2)));
 #ifndef QLA_HLOAD_AUX
 #define QLA_HLOAD_AUX 0
 #endif
+// Plain stores for out: with inputs streamed from HBM they beat
+// non-temporal ones (kv tiles write 64-byte halves of lines that L2 merges).
 #ifndef QLA_STORE_AUX
-#define QLA_STORE_AUX 2  // non-temporal: out is not re-read
+#define QLA_STORE_AUX 0
 #endif
 #ifndef QLA_FWD_DMA
 #define QLA_FWD_DMA 1
 #endif
 #ifndef QLA_DMA_WAVES
 #define QLA_DMA_WAVES 4
+#endif
+// Forward K <= 128: H is loaded this many steps ahead.
+#ifndef QLA_H_AHEAD
+#define QLA_H_AHEAD 3
 #endif
 #ifndef QLA_MO_AHEAD
 #define QLA_MO_AHEAD 2
@@ -727,6 +733,8 @@ struct FwdDma {
     static constexpr int STAGE = K * K;               // floats per M stage
     static constexpr int LDS_FLOATS = S::STATE_FLOATS + 2 * STAGE;
     static constexpr int kDma = K * K / 256;          // 1 KiB copies per M
+    static constexpr int HA = QLA_H_AHEAD;            // H is loaded HA steps ahead
+    static constexpr int HR = HA + 1;                 // H register slots
     static_assert(kDma % PW == 0, "equal producer shares");
     static constexpr unsigned kMatBytes = (unsigned)K * K * 4u;
 
@@ -797,21 +805,21 @@ struct FwdDma {
         if constexpr (B + 1 < BP) blocks<B + 1>(X, L);
     }
 
-    // Step s (LSX = s & 1 selects the H register slot).  Barrier; operand
+    // Step s (LSX = s % HR selects the H register slot).  Barrier; operand
     // reads (first staged M blocks, the other waves' state rows); out of step
     // s-1 and H of step s+1 on the way; the MFMAs; P = Y + X(H_j) into the
     // next state slot and the own-row registers.
     template <int LSX>
-    static __device__ __forceinline__ void step(int s, Ctx& X, const Chain& C, f4 (&h)[2][T], float* lds,
+    static __device__ __forceinline__ void step(int s, Ctx& X, const Chain& C, f4 (&h)[HR][T], float* lds,
                                                 const Lane& L)
     {
         s = __builtin_amdgcn_readfirstlane(s);  // uniform: keeps the step's descriptors scalar
         float* nxt = lds + ((s + 1) & 1) * (kTileV * LS);
         const int jp = s > 0 ? Tl::seg(C, s - 1) : 0;
         X.out_prev = rsrc(C.out + (size_t)jp * (L.state_bytes / 4), s > 0 ? L.state_bytes : 0u);
-        const bool live = s + 1 < C.n_seg;
+        const bool live = s + HA < C.n_seg;
         const __amdgpu_buffer_rsrc_t Hr =
-            rsrc(C.H + (size_t)(live ? Tl::seg(C, s + 1) : 0) * (L.state_bytes / 4), live ? L.state_bytes : 0u);
+            rsrc(C.H + (size_t)(live ? Tl::seg(C, s + HA) : 0) * (L.state_bytes / 4), live ? L.state_bytes : 0u);
 
         __builtin_amdgcn_sched_barrier(0);
         lds_handoff();
@@ -832,10 +840,10 @@ struct FwdDma {
         // memory queue, and a load or store waiting for a slot there would
         // hold up this wave's MFMAs.
         Tl::store_state(X.out_prev, X.own, L);
-        Tl::load_state(h[(LSX + 1) & 1], Hr, L);
+        Tl::load_state(h[(LSX + HA) % HR], Hr, L);
 
         f4 hx[T];
-        Tl::frag_from_vecs(hx, h[LSX & 1]);
+        Tl::frag_from_vecs(hx, h[LSX]);
 #pragma unroll
         for (int t = 0; t < T; ++t) X.acc[t] += hx[t];
         debug_delay(L.wave, s, 1);
@@ -845,24 +853,44 @@ struct FwdDma {
         __builtin_amdgcn_sched_barrier(0);
     }
 
+    template <int LSX>
+    static __device__ __forceinline__ void tail(int s, Ctx& X, const Chain& C, f4 (&h)[HR][T], float* lds,
+                                                const Lane& L)
+    {
+        if constexpr (LSX < HR - 1) {
+            if (s + LSX < C.n_seg) {
+                step<LSX>(s + LSX, X, C, h, lds, L);
+                tail<LSX + 1>(s, X, C, h, lds, L);
+            }
+        }
+    }
+
     static __device__ __forceinline__ void consumer(const Chain& C, const float* S0, float* lds, size_t chain,
                                                     int tile, int V)
     {
         const Lane L = Tl::make_lane(tile * kTileV, V);
         const size_t state = (size_t)K * V;
         Ctx X;
-        f4 h[2][T];
+        f4 h[HR][T];
         f4 sv[T];
         Tl::load_state(sv, rsrc(S0 ? S0 + chain * state : C.H, S0 ? L.state_bytes : 0u), L);
-        Tl::load_state(h[0], rsrc(C.H + (size_t)Tl::seg(C, 0) * (L.state_bytes / 4), L.state_bytes), L);
+#pragma unroll
+        for (int i = 0; i < HA; ++i) {
+            const bool live = i < C.n_seg;
+            Tl::load_state(h[i], rsrc(C.H + (size_t)Tl::seg(C, live ? i : 0) * (L.state_bytes / 4),
+                                      live ? L.state_bytes : 0u), L);
+        }
         Tl::frag_from_vecs(X.own, sv);
         Tl::put_state(lds, X.own, L);
         int s = 0;
-        for (; s + 2 <= C.n_seg; s += 2) {
+        for (; s + HR <= C.n_seg; s += HR) {
             step<0>(s, X, C, h, lds, L);
-            step<1>(s + 1, X, C, h, lds, L);
+            if constexpr (HR > 1) step<1 % HR>(s + 1, X, C, h, lds, L);
+            if constexpr (HR > 2) step<2 % HR>(s + 2, X, C, h, lds, L);
+            if constexpr (HR > 3) step<3 % HR>(s + 3, X, C, h, lds, L);
+            if constexpr (HR > 4) step<4 % HR>(s + 4, X, C, h, lds, L);
         }
-        if (s < C.n_seg) step<0>(s, X, C, h, lds, L);
+        tail<0>(s, X, C, h, lds, L);
         Tl::store_state(rsrc(C.out + (size_t)Tl::seg(C, C.n_seg - 1) * (L.state_bytes / 4), L.state_bytes), X.own,
                         L);
     }

@@ -156,3 +156,19 @@ def coded_states(lead: tuple, n_seg: int, R: int, C: int) -> np.ndarray:
 def decode_code(value) -> tuple:
     x = int(value) - 1
     return x >> 16, (x >> 8) & 255, x & 255
+
+
+# The pages' operator sweep (correction note, section "性能结果"): sequence
+# lengths 4K / 8K / 32K tokens and 4 / 16 / 32 heads, both layouts and
+# directions, with and without an initial state, at K = V = 128.  Segments
+# are 4096 tokens, so the lengths are 1, 2 and 8 segments; batch 1.
+SEG_TOKENS = 4096
+SWEEP_TOKENS = (4096, 8192, 32768)
+SWEEP_HEADS = (4, 16, 32)
+
+
+def sweep_arrays(tokens: int, heads: int):
+    """kv-view (H, M, S0) for one sweep point: the 32K x 32-head recipe
+    (M = 0.9 I + N(0, 0.1/K), H and S0 ~ N(0, 1)) at its own seed."""
+    ti, hi = SWEEP_TOKENS.index(tokens), SWEEP_HEADS.index(heads)
+    return random_case(60 + 3 * ti + hi, (1, heads), tokens // SEG_TOKENS, 128, 128, 0.9, 0.1, True)
