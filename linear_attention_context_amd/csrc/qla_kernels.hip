@@ -76,9 +76,13 @@ typedef unsigned u2 __attribute__((ext_vector_type(2)));
 #ifndef QLA_DMA_WAVES
 #define QLA_DMA_WAVES 4
 #endif
-// Forward K <= 128: H is loaded this many steps ahead.
+// Forward K <= 128: H is loaded this many steps ahead, and M_j's lines are
+// touched into L2 this many steps ahead of its copy (0: off).
 #ifndef QLA_H_AHEAD
 #define QLA_H_AHEAD 3
+#endif
+#ifndef QLA_M_TOUCH
+#define QLA_M_TOUCH 2
 #endif
 #ifndef QLA_MO_AHEAD
 #define QLA_MO_AHEAD 2
@@ -743,10 +747,28 @@ struct FwdDma {
         f4 own[T];
         f4 pv[K / 16];
         f4 mo[MA + 1][T];
+        float touched[2];  // cache warm-up loads of the last two steps
         const float* cur;
         const float* st;
         __amdgpu_buffer_rsrc_t out_prev;
+        int tile, tiles;
     };
+
+    // L2 warm-up of M_j ahead of its copy.  The chain's workgroups sit on one
+    // XCD and copy the same M_j; together they touch each of its 128-byte
+    // lines once (one 4-byte load per line: MFMA wave w of tile t takes lines
+    // t + tiles*(w + CW*lane)), so the copy that follows hits in L2 instead of
+    // waiting on HBM.  The loaded value is consumed two steps later, when the
+    // wait the compiler places for it is long satisfied; lanes past the end
+    // use an out-of-range offset and touch nothing.
+    static constexpr int kLines = K * K * 4 / 128;
+    static __device__ __forceinline__ float touch(const Chain& C, int s, const Ctx& X, const Lane& L)
+    {
+        const bool live = QLA_M_TOUCH > 0 && s < C.n_seg;
+        const __amdgpu_buffer_rsrc_t r = rsrc(C.M + (size_t)Tl::seg(C, live ? s : 0) * K * K, live ? kMatBytes : 0u);
+        const int line = X.tile + X.tiles * (L.wave + CW * (int)(threadIdx.x & 63));
+        return bload1(r, line < kLines ? 128u * (unsigned)line : kOutOfRange);
+    }
 
     // ---- producer ---------------------------------------------------------
     // Copy M_j into a stage: copy i fills stage floats [256 i, 256 i + 256);
@@ -841,6 +863,10 @@ struct FwdDma {
         // hold up this wave's MFMAs.
         Tl::store_state(X.out_prev, X.own, L);
         Tl::load_state(h[(LSX + HA) % HR], Hr, L);
+        if constexpr (QLA_M_TOUCH > 0) {
+            asm volatile("" ::"v"(X.touched[LSX & 1]));
+            X.touched[LSX & 1] = touch(C, s + QLA_M_TOUCH + 1, X, L);
+        }
 
         f4 hx[T];
         Tl::frag_from_vecs(hx, h[LSX]);
@@ -871,6 +897,8 @@ struct FwdDma {
         const Lane L = Tl::make_lane(tile * kTileV, V);
         const size_t state = (size_t)K * V;
         Ctx X;
+        X.tile = tile;
+        X.tiles = (V + kTileV - 1) / kTileV;
         f4 h[HR][T];
         f4 sv[T];
         Tl::load_state(sv, rsrc(S0 ? S0 + chain * state : C.H, S0 ? L.state_bytes : 0u), L);
@@ -882,6 +910,9 @@ struct FwdDma {
         }
         Tl::frag_from_vecs(X.own, sv);
         Tl::put_state(lds, X.own, L);
+        // Warm-up of the units whose copies come before the steps' own touches.
+        X.touched[0] = QLA_M_TOUCH > 1 ? touch(C, 2, X, L) : 0.f;
+        X.touched[1] = QLA_M_TOUCH > 0 ? touch(C, 1, X, L) : 0.f;
         int s = 0;
         for (; s + HR <= C.n_seg; s += HR) {
             step<0>(s, X, C, h, lds, L);
