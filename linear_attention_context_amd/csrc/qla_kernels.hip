@@ -484,6 +484,10 @@ struct Tile {
         }
     }
 
+    static constexpr int kLinesT = K * K * 4 / 128;  // 128-byte lines of one M
+    static constexpr int kTouchT = (kLinesT + 64 * S::WAVES - 1) / (64 * S::WAVES);
+    static constexpr int TD = (D + NP - 1) / NP + 2;  // steps ahead of the touch
+
     // Working registers, carried from step to step.
     struct StepCtx {
         f4 acc[T];
@@ -495,7 +499,27 @@ struct Tile {
         const float* st_cur;
         float* st_next;
         __amdgpu_buffer_rsrc_t out_prev;  // out_j of the previous step (empty at step 0)
+        float touched[F][kTouchT];        // cache warm-up loads, consumed F steps later
+        int tile, tiles;
     };
+
+    // L2 warm-up of M ahead of the register prefetch (which runs D units, so
+    // D / NP steps, ahead): in step s the waves of the chain's workgroups touch
+    // each 128-byte line of M for step s + TD once (one 4-byte load per line:
+    // wave w of tile t takes lines t + tiles*(w + WAVES*(lane + 64k))).  The
+    // value is consumed F steps later, when the compiler's wait for it is long
+    // satisfied; lanes past the end use an out-of-range offset.
+    static __device__ __forceinline__ void touch_ahead(float (&y)[kTouchT], const Chain& C, int s, const StepCtx& X,
+                                                       const Lane& L)
+    {
+        const bool live = QLA_M_TOUCH > 0 && s < C.n_seg;
+        const __amdgpu_buffer_rsrc_t r = rsrc(C.M + (size_t)seg(C, live ? s : 0) * K * K, live ? kMatBytes : 0u);
+#pragma unroll
+        for (int k = 0; k < kTouchT; ++k) {
+            const int line = X.tile + X.tiles * (L.wave + S::WAVES * ((int)(threadIdx.x & 63) + 64 * k));
+            y[k] = bload1(r, line < kLinesT ? 128u * (unsigned)line : kOutOfRange);
+        }
+    }
 
     // The staged M operand of a panel's first MA blocks.
     static __device__ __forceinline__ void read_mo_head(f4 (&mh)[MA][T], const float* st, const Lane& L)
@@ -634,6 +658,11 @@ struct Tile {
         put_state(nxt, X.acc, L);
 #pragma unroll
         for (int t = 0; t < T; ++t) X.own[t] = X.acc[t];
+        if constexpr (QLA_M_TOUCH > 0) {
+#pragma unroll
+            for (int k = 0; k < kTouchT; ++k) asm volatile("" ::"v"(X.touched[LSX][k]));
+            touch_ahead(X.touched[LSX], C, s + TD, X, L);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -677,6 +706,12 @@ struct Tile {
         f4 m[R][T][BP];
         f4 h[RH][T];
         StepCtx X;
+        X.tile = tile;
+        X.tiles = (V + kTileV - 1) / kTileV;
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+#pragma unroll
+            for (int k = 0; k < kTouchT; ++k) X.touched[i][k] = 0.f;
         // Prologue.  A CU's vector memory path takes about 64 bytes per clock,
         // and a wave stalls at a load it cannot queue, so the loads go out in
         // the order they are needed: the initial state and the first unit of
