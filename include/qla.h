@@ -73,9 +73,15 @@ extern "C" {
 #define QLA_ERR_LAUNCH (-7) /* the runtime rejected the launch */
 #define QLA_ERR_MEMORY (-8) /* a pointer is not device memory, or the extent the
                                call needs runs past the end of its allocation */
+#define QLA_ERR_SEQS (-9)   /* segment offsets of a variable-length call: NULL, more
+                               than QLA_MAX_SEQS sequences, not starting at 0, or
+                               decreasing */
 
 /* Largest number of head groups one grouped call accepts. */
 #define QLA_MAX_GROUPS 64
+
+/* Largest number of sequences one variable-length call accepts. */
+#define QLA_MAX_SEQS 256
 
 /* One head group of a grouped call: heads [head_begin, head_begin+head_count)
  * of every batch entry use this layout and direction. */
@@ -117,6 +123,32 @@ QLA_API int qla_correct_h0(const float* H, const float* M, const float* S0, floa
 QLA_API int qla_correct_h0_grouped(const float* H, const float* M, const float* S0, float* out,
                            const qla_head_group* groups, int n_groups,
                            int batch, int heads, int n_seg, int K, int V, void* stream);
+
+/*
+ * qla_correct_h0_varlen -- like qla_correct_h0 for n_seqs sequences whose
+ * segment counts differ (the correction note, section "性能结果", benchmarks the
+ * operator on variable-length inputs).  Sequence b has
+ * n_b = seg_offsets[b+1] - seg_offsets[b] segments (n_b >= 0) and `heads`
+ * chains.
+ *   seg_offsets : HOST array of n_seqs + 1 ints, seg_offsets[0] = 0,
+ *                 non-decreasing; copied into the launch, may be freed on
+ *                 return.  0 <= n_seqs <= QLA_MAX_SEQS.
+ *   H, out      : sequences back to back, sequence b's block starting at
+ *                 segment heads * seg_offsets[b] (i.e. at float
+ *                 heads * seg_offsets[b] * K * V) and laid out
+ *                 [heads][n_b][K][V] (kv) or [heads][n_b][V][K] (vk); in
+ *                 total heads * seg_offsets[n_seqs] segment states.
+ *   M           : the same with K x K matrices.
+ *   S0          : [n_seqs][heads][K][V] (kv) or [..][V][K] (vk), or NULL.
+ * With every n_b equal to n this is exactly qla_correct_h0 with batch =
+ * n_seqs and n_seg = n.  A sequence with n_b = 0 reads and writes nothing;
+ * a call with no segments at all is an empty call (QLA_OK, nothing
+ * enqueued).  Bad offsets return QLA_ERR_SEQS; other arguments, checks and
+ * the return value are as for qla_correct_h0.
+ */
+QLA_API int qla_correct_h0_varlen(const float* H, const float* M, const float* S0, float* out,
+                          int layout, int direction, const int* seg_offsets, int n_seqs,
+                          int heads, int K, int V, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 QLA_API const char* qla_status_str(int status);

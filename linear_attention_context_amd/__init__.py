@@ -26,6 +26,7 @@ QLA_MAX_GROUPS = 64
 STATUS = {
     0: "QLA_OK", -1: "QLA_ERR_NULL", -2: "QLA_ERR_ENUM", -3: "QLA_ERR_SHAPE", -4: "QLA_ERR_ALIGN",
     -5: "QLA_ERR_ALIAS", -6: "QLA_ERR_GROUPS", -7: "QLA_ERR_LAUNCH", -8: "QLA_ERR_MEMORY",
+    -9: "QLA_ERR_SEQS",
 }
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -65,6 +66,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.qla_correct_h0_grouped.argtypes = [vp, vp, vp, vp, ctypes.POINTER(qla_head_group), ci,
                                            ci, ci, ci, ci, ci, vp]
     lib.qla_correct_h0_grouped.restype = ci
+    lib.qla_correct_h0_varlen.argtypes = [vp, vp, vp, vp, ci, ci, ctypes.POINTER(ci), ci, ci, ci, ci, vp]
+    lib.qla_correct_h0_varlen.restype = ci
     lib.qla_status_str.argtypes = [ci]
     lib.qla_status_str.restype = ctypes.c_char_p
     _libs[path] = lib
@@ -144,5 +147,31 @@ def qla_correct_h0_grouped(H, M, S0, out, groups, batch, heads, n_seg, K, V, str
                            lib: ctypes.CDLL | None = None) -> None:
     lib = lib or load_library()
     rc = raw_correct_h0_grouped(H, M, S0, out, groups, batch, heads, n_seg, K, V, stream, lib)
+    if rc != 0:
+        raise QlaError(rc, qla_status_str(rc, lib))
+
+
+def raw_correct_h0_varlen(H, M, S0, out, layout, direction, seg_offsets, heads, K, V, stream=None,
+                          lib: ctypes.CDLL | None = None, n_seqs: int | None = None) -> int:
+    """Call qla_correct_h0_varlen; ``seg_offsets`` is a sequence of n_seqs + 1 ints
+    (host memory), or None to pass a NULL pointer."""
+    lib = lib or load_library()
+    if seg_offsets is None:
+        arr, n = None, (0 if n_seqs is None else n_seqs)
+    else:
+        offs = [int(x) for x in seg_offsets]
+        arr = (ctypes.c_int * max(len(offs), 1))(*offs)
+        n = len(offs) - 1 if n_seqs is None else n_seqs
+    return lib.qla_correct_h0_varlen(_ptr(H), _ptr(M), _ptr(S0), _ptr(out),
+                                     _enum(layout, _LAYOUT_NAMES), _enum(direction, _DIR_NAMES),
+                                     arr, n, heads, K, V, _stream(stream))
+
+
+def qla_correct_h0_varlen(H, M, S0, out, layout, direction, seg_offsets, heads, K, V, stream=None,
+                          lib: ctypes.CDLL | None = None) -> None:
+    """Variable-length chains: sequence b has seg_offsets[b+1] - seg_offsets[b]
+    segments; raises QlaError on a non-zero status."""
+    lib = lib or load_library()
+    rc = raw_correct_h0_varlen(H, M, S0, out, layout, direction, seg_offsets, heads, K, V, stream, lib)
     if rc != 0:
         raise QlaError(rc, qla_status_str(rc, lib))

@@ -55,16 +55,17 @@ int check_memory(const void* p, size_t bytes)
     return QLA_OK;
 }
 
-// Checks shared by both entry points once the shape is known to be valid and
-// the call non-empty.
+// Checks shared by the entry points once the shape is known to be valid and
+// the call non-empty: `segments` states of H / M / out in total, `chains`
+// initial states.
 int check_buffers(const float* H, const float* M, const float* S0, const float* out, long long chains,
-                  int n_seg, int K, int V)
+                  long long segments, int K, int V)
 {
     if (!H || !M || !out) return QLA_ERR_NULL;
     if (!aligned16(H) || !aligned16(M) || !aligned16(out) || (S0 && !aligned16(S0))) return QLA_ERR_ALIGN;
     const size_t state = (size_t)K * V * sizeof(float);
-    const size_t hbytes = (size_t)chains * n_seg * state;
-    const size_t mbytes = (size_t)chains * n_seg * K * K * sizeof(float);
+    const size_t hbytes = (size_t)segments * state;
+    const size_t mbytes = (size_t)segments * K * K * sizeof(float);
     const size_t sbytes = (size_t)chains * state;
     const Extent eo = extent(out, hbytes);
     if (out != H && overlap(eo, extent(H, hbytes))) return QLA_ERR_ALIAS;
@@ -90,7 +91,7 @@ int qla_correct_h0(const float* H, const float* M, const float* S0, float* out, 
     if (rc != QLA_OK) return rc;
     const long long chains = (long long)batch * heads;
     if (chains == 0 || n_seg == 0) return QLA_OK;
-    if ((rc = check_buffers(H, M, S0, out, chains, n_seg, K, V)) != QLA_OK) return rc;
+    if ((rc = check_buffers(H, M, S0, out, chains, chains * n_seg, K, V)) != QLA_OK) return rc;
 
     qla::LaunchArgs a{H, M, S0, out, layout, direction, chains, heads, n_seg, K, V, stream};
     return qla::launch_correct_h0(a) == hipSuccess ? QLA_OK : QLA_ERR_LAUNCH;
@@ -129,10 +130,35 @@ int qla_correct_h0_grouped(const float* H, const float* M, const float* S0, floa
 
     const long long chains = (long long)batch * heads;
     if (chains == 0 || n_seg == 0) return QLA_OK;
-    if ((rc = check_buffers(H, M, S0, out, chains, n_seg, K, V)) != QLA_OK) return rc;
+    if ((rc = check_buffers(H, M, S0, out, chains, chains * n_seg, K, V)) != QLA_OK) return rc;
 
     qla::LaunchArgs a{H, M, S0, out, -1, -1, chains, heads, n_seg, K, V, stream};
     return qla::launch_correct_h0_grouped(a, table) == hipSuccess ? QLA_OK : QLA_ERR_LAUNCH;
+}
+
+int qla_correct_h0_varlen(const float* H, const float* M, const float* S0, float* out, int layout, int direction,
+                          const int* seg_offsets, int n_seqs, int heads, int K, int V, void* stream)
+{
+    if (!valid_layout(layout) || !valid_direction(direction)) return QLA_ERR_ENUM;
+    if (!seg_offsets || n_seqs < 0 || n_seqs > QLA_MAX_SEQS || seg_offsets[0] != 0) return QLA_ERR_SEQS;
+    qla::SeqTable seqs{};
+    seqs.n = n_seqs;
+    seqs.offs[0] = 0;
+    for (int b = 0; b < n_seqs; ++b) {
+        if (seg_offsets[b + 1] < seg_offsets[b]) return QLA_ERR_SEQS;
+        seqs.offs[b + 1] = seg_offsets[b + 1];
+    }
+    int rc = check_shape(n_seqs, heads, 0, K, V);
+    if (rc != QLA_OK) return rc;
+    const long long chains = (long long)n_seqs * heads;
+    const long long segments = (long long)heads * seg_offsets[n_seqs];
+    // Segment offsets inside the kernel are int: heads * offset must fit.
+    if ((long long)heads * seg_offsets[n_seqs] > INT32_MAX) return QLA_ERR_SHAPE;
+    if (chains == 0 || segments == 0) return QLA_OK;
+    if ((rc = check_buffers(H, M, S0, out, chains, segments, K, V)) != QLA_OK) return rc;
+
+    qla::LaunchArgs a{H, M, S0, out, layout, direction, chains, heads, -1, K, V, stream};
+    return qla::launch_correct_h0_varlen(a, seqs) == hipSuccess ? QLA_OK : QLA_ERR_LAUNCH;
 }
 
 const char* qla_status_str(int status)
@@ -148,6 +174,8 @@ const char* qla_status_str(int status)
     case QLA_ERR_GROUPS: return "head groups do not partition [0, heads) (or too many groups)";
     case QLA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
     case QLA_ERR_MEMORY: return "a buffer is not device memory or is smaller than the call needs";
+    case QLA_ERR_SEQS: return "segment offsets are NULL, not starting at 0, decreasing, or for more than "
+                              "QLA_MAX_SEQS sequences";
     default: return "unknown status";
     }
 }

@@ -34,8 +34,16 @@ struct GroupTable {
     int variant[QLA_MAX_GROUPS];
 };
 
+// Segment offsets of a variable-length call, copied by value into the
+// kernel's arguments: sequence b has offs[b+1] - offs[b] segments.
+struct SeqTable {
+    int n;
+    int offs[QLA_MAX_SEQS + 1];
+};
+
 int tiles_for(int V);
 hipError_t launch_correct_h0(const LaunchArgs& a);
 hipError_t launch_correct_h0_grouped(const LaunchArgs& a, const GroupTable& table);
+hipError_t launch_correct_h0_varlen(const LaunchArgs& a, const SeqTable& seqs);
 
 }  // namespace qla

@@ -695,13 +695,24 @@ struct Tile {
         }
     }
 
+    // Chain `chain` of a call whose chains all have n_seg segments.
     static __device__ __forceinline__ void run(const float* H, const float* M, const float* S0, float* out,
                                                int n_seg, int V, size_t chain, int tile, float* lds)
     {
-        const Lane L = make_lane(tile * kTileV, V);
         const size_t state = (size_t)K * V;
         const Chain C{M + chain * (size_t)n_seg * K * K, H + chain * state * n_seg, out + chain * state * n_seg,
                       n_seg};
+        run_chain(C, S0 ? S0 + chain * state : nullptr, V, tile, lds);
+    }
+
+    // One chain given by its base pointers and segment count; S0c is its
+    // initial state or NULL.  A chain without segments runs no step: every
+    // global access below is then out of its buffer resource's range and
+    // does nothing (kept branch-free: an early return here costs the compiler
+    // its knowledge that the descriptors are uniform).
+    static __device__ __forceinline__ void run_chain(const Chain& C, const float* S0c, int V, int tile, float* lds)
+    {
+        const Lane L = make_lane(tile * kTileV, V);
 
         f4 m[R][T][BP];
         f4 h[RH][T];
@@ -719,7 +730,7 @@ struct Tile {
         // hand-off; only then the rest of the prefetch distance, which the
         // first steps' work covers.
         f4 sv[T];
-        load_state(sv, rsrc(S0 ? S0 + chain * state : H, S0 ? L.state_bytes : 0u), L);
+        load_state(sv, rsrc(S0c ? S0c : C.H, S0c ? L.state_bytes : 0u), L);
         prologue<0, 1>(C, m, h, L);
         frag_from_vecs(X.own, sv);
         put_state(lds, X.own, L);
@@ -729,7 +740,7 @@ struct Tile {
         prologue<1, D>(C, m, h, L);
 
         int s = 0;
-        for (; s + F <= n_seg; s += F) {
+        for (; s + F <= C.n_seg; s += F) {
             step<0>(s, X, C, m, h, lds, L);
             if constexpr (F > 1) step<1 % F>(s + 1, X, C, m, h, lds, L);
             if constexpr (F > 2) step<2 % F>(s + 2, X, C, m, h, lds, L);
@@ -737,8 +748,10 @@ struct Tile {
             if constexpr (F > 4) step<4 % F>(s + 4, X, C, m, h, lds, L);
             if constexpr (F > 5) step<5 % F>(s + 5, X, C, m, h, lds, L);
         }
-        tail<0>(s, n_seg - s, X, C, m, h, lds, L);
-        store_state(rsrc(C.out + (size_t)seg(C, n_seg - 1) * (L.state_bytes / 4), L.state_bytes), X.own, L);
+        tail<0>(s, C.n_seg - s, X, C, m, h, lds, L);
+        const bool any = C.n_seg > 0;
+        store_state(rsrc(C.out + (size_t)seg(C, any ? C.n_seg - 1 : 0) * (L.state_bytes / 4), any ? L.state_bytes : 0u),
+                    X.own, L);
     }
 };
 
@@ -926,17 +939,15 @@ struct FwdDma {
         }
     }
 
-    static __device__ __forceinline__ void consumer(const Chain& C, const float* S0, float* lds, size_t chain,
-                                                    int tile, int V)
+    static __device__ __forceinline__ void consumer(const Chain& C, const float* S0c, float* lds, int tile, int V)
     {
         const Lane L = Tl::make_lane(tile * kTileV, V);
-        const size_t state = (size_t)K * V;
         Ctx X;
         X.tile = tile;
         X.tiles = (V + kTileV - 1) / kTileV;
         f4 h[HR][T];
         f4 sv[T];
-        Tl::load_state(sv, rsrc(S0 ? S0 + chain * state : C.H, S0 ? L.state_bytes : 0u), L);
+        Tl::load_state(sv, rsrc(S0c ? S0c : C.H, S0c ? L.state_bytes : 0u), L);
 #pragma unroll
         for (int i = 0; i < HA; ++i) {
             const bool live = i < C.n_seg;
@@ -967,9 +978,16 @@ struct FwdDma {
         const size_t state = (size_t)K * V;
         const Chain C{M + chain * (size_t)n_seg * K * K, H + chain * state * n_seg, out + chain * state * n_seg,
                       n_seg};
+        run_chain(C, S0 ? S0 + chain * state : nullptr, V, tile, lds);
+    }
+
+    static __device__ __forceinline__ void run_chain(const Chain& C, const float* S0c, int V, int tile, float* lds)
+    {
+        // A chain without segments: every wave leaves before any barrier.
+        if (__builtin_amdgcn_readfirstlane(C.n_seg) <= 0) return;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         if (wave >= CW) producer(C, lds, wave - CW);
-        else consumer(C, S0, lds, chain, tile, V);
+        else consumer(C, S0c, lds, tile, V);
     }
 };
 
@@ -1013,6 +1031,49 @@ __global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void cor
     D::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds);
 }
 
+// Variable-length chains: sequence b has offs[b+1] - offs[b] segments; its
+// block of H / M / out starts at segment heads * offs[b] and holds its heads'
+// chains back to back, so chain (b, h) starts at segment heads * offs[b] +
+// h * n_b.  S0 is [n_seqs][heads][K][V] as usual.
+template <typename Chain, int K>
+__device__ __forceinline__ Chain varlen_chain(const float* H, const float* M, float* out, int heads, int V, int chain,
+                                              const SeqTable& seqs)
+{
+    const int b = chain / heads, h = chain - b * heads;
+    const int n = seqs.offs[b + 1] - seqs.offs[b];
+    const size_t base = (size_t)heads * seqs.offs[b] + (size_t)h * n;  // in segments
+    const size_t state = (size_t)K * V;
+    return Chain{M + base * K * K, H + base * state, out + base * state, n};
+}
+
+template <int K, int LAYOUT, int DIR>
+__global__ __launch_bounds__(64 * QLA_WAVES(K, DIR == QLA_DIR_FWD)) void correct_h0_varlen_kernel(
+    const float* H, const float* __restrict__ M, const float* S0, float* out, int heads, int V, int tiles,
+    SeqTable seqs)
+{
+    using Tl = typename Plain<K, LAYOUT, DIR>::Tl;
+    __shared__ __attribute__((aligned(16))) float lds[Tl::LDS_FLOATS];
+    const int id = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int chain = id / tiles;
+    const int tile = id - chain * tiles;
+    const auto C = varlen_chain<typename Tl::Chain, K>(H, M, out, heads, V, chain, seqs);
+    Tl::run_chain(C, S0 ? S0 + (size_t)chain * K * V : nullptr, V, tile, lds);
+}
+
+template <int K, int LAYOUT>
+__global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void correct_h0_fwd_dma_varlen_kernel(
+    const float* H, const float* __restrict__ M, const float* S0, float* out, int heads, int V, int tiles,
+    SeqTable seqs)
+{
+    using D = FwdDma<K, LAYOUT>;
+    __shared__ __attribute__((aligned(16))) float lds[D::LDS_FLOATS];
+    const int id = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int chain = id / tiles;
+    const int tile = id - chain * tiles;
+    const auto C = varlen_chain<typename D::Chain, K>(H, M, out, heads, V, chain, seqs);
+    D::run_chain(C, S0 ? S0 + (size_t)chain * K * V : nullptr, V, tile, lds);
+}
+
 template <int K>
 __global__ __launch_bounds__(64 * QLA_GROUPED_WAVES(K)) void correct_h0_grouped_kernel(
     const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles, int heads,
@@ -1043,13 +1104,12 @@ hipError_t launch_one(const LaunchArgs& a)
     const int tiles = (a.V + kTileV - 1) / kTileV;
     const dim3 grid((unsigned)(a.chains * tiles));
     if constexpr (QLA_FWD_DMA && DIR == QLA_DIR_FWD && K <= 128) {
-        hipLaunchKernelGGL((correct_h0_fwd_dma_kernel<K, LAYOUT>), grid, dim3(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)), 0,
+        hipLaunchKernelGGL((correct_h0_fwd_dma_kernel<K, LAYOUT>), grid, dim3(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)),
+                           0, (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles);
+    } else {
+        hipLaunchKernelGGL((correct_h0_kernel<K, LAYOUT, DIR>), grid, dim3(64 * Plain<K, LAYOUT, DIR>::WAVES), 0,
                            (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles);
-        return hipGetLastError();
     }
-    hipLaunchKernelGGL((correct_h0_kernel<K, LAYOUT, DIR>), grid, dim3(64 * Plain<K, LAYOUT, DIR>::WAVES), 0,
-                       (hipStream_t)a.stream, a.H,
-                       a.M, a.S0, a.out, a.n_seg, a.V, tiles);
     return hipGetLastError();
 }
 
@@ -1061,6 +1121,32 @@ hipError_t launch_k(const LaunchArgs& a)
                                           : launch_one<K, QLA_LAYOUT_KV, QLA_DIR_BWD>(a);
     return a.direction == QLA_DIR_FWD ? launch_one<K, QLA_LAYOUT_VK, QLA_DIR_FWD>(a)
                                       : launch_one<K, QLA_LAYOUT_VK, QLA_DIR_BWD>(a);
+}
+
+template <int K, int LAYOUT, int DIR>
+hipError_t launch_varlen_one(const LaunchArgs& a, const SeqTable& seqs)
+{
+    const int tiles = (a.V + kTileV - 1) / kTileV;
+    const dim3 grid((unsigned)(a.chains * tiles));
+    if constexpr (QLA_FWD_DMA && DIR == QLA_DIR_FWD && K <= 128) {
+        hipLaunchKernelGGL((correct_h0_fwd_dma_varlen_kernel<K, LAYOUT>), grid,
+                           dim3(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)), 0, (hipStream_t)a.stream, a.H, a.M, a.S0,
+                           a.out, a.heads, a.V, tiles, seqs);
+    } else {
+        hipLaunchKernelGGL((correct_h0_varlen_kernel<K, LAYOUT, DIR>), grid, dim3(64 * Plain<K, LAYOUT, DIR>::WAVES),
+                           0, (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.heads, a.V, tiles, seqs);
+    }
+    return hipGetLastError();
+}
+
+template <int K>
+hipError_t launch_varlen_k(const LaunchArgs& a, const SeqTable& seqs)
+{
+    if (a.layout == QLA_LAYOUT_KV)
+        return a.direction == QLA_DIR_FWD ? launch_varlen_one<K, QLA_LAYOUT_KV, QLA_DIR_FWD>(a, seqs)
+                                          : launch_varlen_one<K, QLA_LAYOUT_KV, QLA_DIR_BWD>(a, seqs);
+    return a.direction == QLA_DIR_FWD ? launch_varlen_one<K, QLA_LAYOUT_VK, QLA_DIR_FWD>(a, seqs)
+                                      : launch_varlen_one<K, QLA_LAYOUT_VK, QLA_DIR_BWD>(a, seqs);
 }
 
 template <int K>
@@ -1084,6 +1170,16 @@ hipError_t launch_correct_h0(const LaunchArgs& a)
     case 64: return launch_k<64>(a);
     case 128: return launch_k<128>(a);
     case 256: return launch_k<256>(a);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_correct_h0_varlen(const LaunchArgs& a, const SeqTable& seqs)
+{
+    switch (a.K) {
+    case 64: return launch_varlen_k<64>(a, seqs);
+    case 128: return launch_varlen_k<128>(a, seqs);
+    case 256: return launch_varlen_k<256>(a, seqs);
     default: return hipErrorInvalidValue;
     }
 }

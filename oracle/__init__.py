@@ -11,6 +11,11 @@ it computes, and the page sections it follows, are stated in the C file's
 header: the forward pass is S_j = M_j S_{j-1} + H_j, the backward pass
 G_j = M_j^T G_{j+1} + H_j in reverse segment order (kv view), vk stores the
 transposed state and multiplies on the right.
+
+``correct_h0_varlen`` does no arithmetic of its own: it cuts packed ragged
+chains (the variable-length case the correction note's performance section
+benchmarks) out of their buffers and runs each through ``correct_h0``.  Its
+packing is pinned against exact rational results placed chain by chain.
 """
 from __future__ import annotations
 
@@ -111,4 +116,30 @@ def correct_h0(H, M, S0, layout, direction):
         lay, dire, chains, n_seg, K, V)
     if rc != 0:
         raise RuntimeError(f"oracle failed with code {rc}")
+    return out
+
+
+def correct_h0_varlen(H, M, S0, seg_offsets, heads, layout, direction):
+    """Variable-length chains, by slicing: sequence b has
+    n_b = seg_offsets[b+1] - seg_offsets[b] segments, and the packed arrays hold
+    the sequences back to back, sequence b's block starting at segment
+    heads * seg_offsets[b] and laid out [heads][n_b][K][V] (or [..][V][K] for vk);
+    M likewise with K x K; S0 is [n_seqs][heads][..] or None.  Each chain is run
+    through ``correct_h0`` (no arithmetic here).  Returns fp64 out shaped like H.
+
+    H and M are given flattened over the segment axis: H [total, R, C] with
+    total = heads * seg_offsets[-1]; M [total, K, K].
+    """
+    offs = [int(x) for x in seg_offsets]
+    H = np.asarray(H)
+    M = np.asarray(M)
+    out = np.zeros(H.shape, dtype=np.float64)
+    for b in range(len(offs) - 1):
+        n = offs[b + 1] - offs[b]
+        for h in range(heads):
+            lo = heads * offs[b] + h * n
+            if n == 0:
+                continue
+            s0 = None if S0 is None else np.asarray(S0)[b, h]
+            out[lo:lo + n] = correct_h0(H[lo:lo + n], M[lo:lo + n], s0, layout, direction)
     return out

@@ -172,3 +172,26 @@ def sweep_arrays(tokens: int, heads: int):
     (M = 0.9 I + N(0, 0.1/K), H and S0 ~ N(0, 1)) at its own seed."""
     ti, hi = SWEEP_TOKENS.index(tokens), SWEEP_HEADS.index(heads)
     return random_case(60 + 3 * ti + hi, (1, heads), tokens // SEG_TOKENS, 128, 128, 0.9, 0.1, True)
+
+
+
+def varlen_case(seed: int, seg_counts, heads: int, K: int, V: int, with_s0: bool = True):
+    """Packed kv-view inputs for variable-length chains: sequence b (with
+    seg_counts[b] segments) is drawn as ``random_case(seed + b, (heads,), n_b,
+    K, V)`` and the sequences are stored back to back along the segment axis.
+    Returns (H [total, K, V], M [total, K, K], S0 [n_seqs, heads, K, V] or None,
+    seg_offsets) with total = heads * sum(seg_counts)."""
+    offs = [0]
+    for n in seg_counts:
+        offs.append(offs[-1] + int(n))
+    Hs, Ms, S0s = [], [], []
+    for b, n in enumerate(seg_counts):
+        H, M, S0 = random_case(seed + b, (heads,), int(n), K, V, 0.9, 0.1, with_s0)
+        Hs.append(H.reshape(heads * int(n), K, V))
+        Ms.append(M.reshape(heads * int(n), K, K))
+        if with_s0:
+            S0s.append(S0)
+    H = np.concatenate(Hs, axis=0) if Hs else np.zeros((0, K, V), np.float32)
+    M = np.concatenate(Ms, axis=0) if Ms else np.zeros((0, K, K), np.float32)
+    S0 = np.stack(S0s, axis=0) if with_s0 and S0s else None
+    return H, M, S0, offs

@@ -27,8 +27,9 @@ def declared_functions():
     return re.findall(r"QLA_API\s+[\w\s\*]+?\b(qla_\w+)\s*\(", text)
 
 
-def test_header_declares_three_entry_points():
-    assert sorted(declared_functions()) == ["qla_correct_h0", "qla_correct_h0_grouped", "qla_status_str"]
+def test_header_declares_four_entry_points():
+    assert sorted(declared_functions()) == ["qla_correct_h0", "qla_correct_h0_grouped",
+                                            "qla_correct_h0_varlen", "qla_status_str"]
 
 
 @pytest.mark.parametrize("variant", ["", "delay"])
@@ -132,3 +133,48 @@ def test_binding_raises_with_status(lib):
     with pytest.raises(qla.QlaError) as e:
         qla.qla_correct_h0(A, A + 0x10000000, None, A + 0x20000000, 0, 0, 1, 1, 1, 96, 64, stream=0)
     assert e.value.status == -3
+
+
+def varlen_call(offs, heads=2, n_seqs=None, **kw):
+    args = dict(H=A, M=A + 0x10000000, S0=None, out=A + 0x20000000, layout=0, direction=0,
+                seg_offsets=offs, heads=heads, K=64, V=64, stream=0, n_seqs=n_seqs)
+    args.update(kw)
+    return qla.raw_correct_h0_varlen(**args)
+
+
+@pytest.mark.parametrize("offs,n_seqs", [
+    (None, 2),                 # NULL offsets
+    ([1, 3, 5], None),         # first offset not zero
+    ([0, 3, 2], None),         # decreasing
+    ([0, 3], -1),              # negative count
+    ([0] * 258, 257),          # above the sequence limit
+])
+def test_varlen_offset_errors(lib, offs, n_seqs):
+    assert varlen_call(offs, n_seqs=n_seqs) == -9
+
+
+def test_varlen_enum_and_shape_errors(lib):
+    assert varlen_call([0, 2], layout=2) == -2
+    assert varlen_call([0, 2], direction=5) == -2
+    assert varlen_call([0, 2], K=96) == -3
+    assert varlen_call([0, 2], heads=-1) == -3
+    assert varlen_call([0, 2 ** 28], heads=16) == -3       # heads * total > INT32_MAX
+
+
+def test_varlen_empty_calls_ok(lib):
+    assert varlen_call([0], H=None, M=None, out=None) == 0              # no sequences
+    assert varlen_call([0, 0, 0], H=None, M=None, out=None) == 0        # all empty
+    assert varlen_call([0, 4], heads=0, H=None, M=None, out=None) == 0  # no heads
+
+
+def test_varlen_null_alignment_alias(lib):
+    assert varlen_call([0, 2, 5], H=None) == -1
+    assert varlen_call([0, 2, 5], out=None) == -1
+    assert varlen_call([0, 2, 5], H=A + 4) == -4
+    assert varlen_call([0, 2, 5], out=A + 16) == -5
+
+
+def test_varlen_binding_raises(lib):
+    with pytest.raises(qla.QlaError) as e:
+        qla.qla_correct_h0_varlen(A, A + 0x10000000, None, A + 0x20000000, 0, 0, [1, 2], 1, 64, 64, stream=0)
+    assert e.value.status == -9
