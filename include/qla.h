@@ -141,7 +141,8 @@ QLA_API int qla_correct_h0_grouped(const float* H, const float* M, const float* 
  *   M           : the same with K x K matrices.
  *   S0          : [n_seqs][heads][K][V] (kv) or [..][V][K] (vk), or NULL.
  * With every n_b equal to n this is exactly qla_correct_h0 with batch =
- * n_seqs and n_seg = n.  A sequence with n_b = 0 reads and writes nothing;
+ * n_seqs and n_seg = n.  A sequence with n_b = 0 writes nothing (its S0
+ * may still be read);
  * a call with no segments at all is an empty call (QLA_OK, nothing
  * enqueued).  Bad offsets return QLA_ERR_SEQS; other arguments, checks and
  * the return value are as for qla_correct_h0.
