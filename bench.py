@@ -43,6 +43,11 @@ PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_context_amd", "csrc", "qla_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "correct_h0_fwd_32k32h_traffic.md")
+# The correction note (Antarx Memos), performance section, table of the 32K x
+# 32-head correction kernel: per-call latency of the final (membar) scheme on
+# an H100, timed as a graph of 16 calls.  Another machine and unstated head
+# dims: context for the same-protocol figure below, not a target.
+PAGES_H100_US = {"kv_fwd": 27.282, "vk_fwd": 29.812}
 
 
 def parse_args(argv=None):
@@ -311,6 +316,28 @@ def main(argv=None):
         warm_us[f"{layout}_{direction}"] = e0.elapsed_time(e1) * 1e3 / nw
     copy_gbps = measured_copy_gbps(torch, dev)
 
+    # Context in the pages' own protocol: a hipGraph of 16 calls on one
+    # resident buffer set, per-call time of its replays.
+    graph_us = {}
+    cap = torch.cuda.Stream()
+    for v, (layout, direction) in enumerate(variants):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap, capture_error_mode="relaxed"):
+            h = torch.cuda.current_stream().cuda_stream
+            for _ in range(16):
+                launch(sets[0][v], h)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 8
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_us[f"{layout}_{direction}"] = e0.elapsed_time(e1) * 1e3 / (16 * reps)
+        del g
+
     per_call_us = {}
     for v, (layout, direction) in enumerate(variants):
         d = per_launch[v]
@@ -356,6 +383,12 @@ def main(argv=None):
         "measured_copy_gbps": copy_gbps,
         "hbm_frac_of_measured_copy": hbm_gbps / copy_gbps,
         "host_us_per_call": host_us,
+        "pages_protocol_context": {
+            "protocol": "hipGraph of 16 calls on one resident buffer set",
+            "us_per_call": graph_us,
+            "h100_us_per_call_pages": PAGES_H100_US,
+            "h100_over_this": {k: PAGES_H100_US[k] / graph_us[k] for k in graph_us if k in PAGES_H100_US},
+        },
         "kernel_source_sha256_16": kernel_source_hash(),
     }
 
