@@ -66,6 +66,9 @@ def parse_args(argv=None):
     p.add_argument("--sweep", action="store_true",
                    help="instead of the step: time the pages' sweep (4K/8K/32K tokens x 4/16/32 heads x "
                         "{kv,vk} x {fwd,bwd} x S0 on/off), one JSON line per point")
+    p.add_argument("--configs", action="store_true",
+                   help="instead of the step: time every workload configuration (tiny, 32K x 32 heads fwd and bwd, "
+                        "long chain, wide grouped), one JSON line per configuration and variant")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for scaling rocprof byte counters)")
     return p.parse_args(argv)
@@ -186,6 +189,73 @@ def run_sweep(args) -> int:
     return 0
 
 
+def run_configs(args) -> int:
+    """Per-call time of each workload configuration and variant, with its
+    algorithmic bytes and FLOP against the roofline: buffer sets rotated so
+    that a call's inputs come from HBM (a single set where one already exceeds
+    the 256 MB MALL), and on one resident set (warm)."""
+    import torch
+
+    import linear_attention_context_amd as qla
+    import qla_inputs as qi
+
+    qla.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    for cfg in sorted(qi.CASES):
+        case = qi.CASES[cfg]
+        B, NH, N, K, V = case.batch, case.heads, case.n_seg, case.K, case.V
+        H, M, S0 = qi.case_arrays(cfg)
+        chains = B * NH
+        nbytes = 4.0 * (chains * N * (2 * K * V + K * K) + (chains * K * V if S0 is not None else 0))
+        flop = chains * N * 2.0 * K * K * V
+        rot = max(1, min(16, -(-(768 << 20) // int(nbytes))))
+        calls = ([("grouped", case.group_heads())] if case.grouped else
+                 [(f"{lay}_{d}", (lay, d)) for lay, d in case.variants])
+        for label, what in calls:
+            if case.grouped:
+                Hl, Sl = H, S0
+            else:
+                Hl = H if what[0] == "kv" else qi.to_vk(H)
+                Sl = None if S0 is None else (S0 if what[0] == "kv" else qi.to_vk(S0))
+            sets = [dict(H=torch.from_numpy(Hl).to(dev), M=torch.from_numpy(M).to(dev),
+                         S0=None if Sl is None else torch.from_numpy(Sl).to(dev),
+                         out=torch.empty(Hl.shape, device=dev)) for _ in range(rot)]
+
+            def call(x):
+                if case.grouped:
+                    qla.qla_correct_h0_grouped(x["H"], x["M"], x["S0"], x["out"], what, B, NH, N, K, V,
+                                               stream=stream.cuda_stream)
+                else:
+                    qla.qla_correct_h0(x["H"], x["M"], x["S0"], x["out"], what[0], what[1], B, NH, N, K, V,
+                                       stream=stream.cuda_stream)
+            reps = 64 if nbytes < (64 << 20) else 8
+            times = {}
+            for kind, order in (("warm", [0] * reps), ("rotated", [i % rot for i in range(max(reps, rot))])):
+                for i in order[:4]:
+                    call(sets[i])
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in order:
+                    call(sets[i])
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times[kind] = e0.elapsed_time(e1) * 1e3 / len(order)
+            t = times["rotated"] * 1e-6
+            t_hbm, t_mfma = nbytes / (PEAK_HBM_GBPS * 1e9), flop / (PEAK_FP32_MFMA_TFLOPS * 1e12)
+            print(json.dumps({
+                "config": cfg, "workload": case.name, "variant": label,
+                "us_per_call": times["rotated"], "warm_us_per_call": times["warm"], "buffer_sets": rot,
+                "corrections_per_s": chains * N / t, "hbm_gbps": nbytes / t / 1e9, "tflops": flop / t / 1e12,
+                "bound": "hbm" if t_hbm > t_mfma else "mfma", "roofline_frac": max(t_hbm, t_mfma) / t,
+                "algorithmic_bytes": nbytes, "flop": flop,
+            }), flush=True)
+            del sets
+            torch.cuda.empty_cache()
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -195,6 +265,8 @@ def main(argv=None):
 
     if args.sweep:
         return run_sweep(args)
+    if args.configs:
+        return run_configs(args)
 
     import torch
 
@@ -427,6 +499,30 @@ def main(argv=None):
             "kind": "oracle",
             "sample": f"the full step (kv fwd + vk fwd, {corrections_per_step} corrections) repeated {reps}x "
                       f"in {el:.1f} s, fp64 plain loops, 1 thread",
+        }
+        # Context: the same oracle over all host cores, one thread per group of
+        # chains (its C loops release the interpreter lock).
+        from concurrent.futures import ThreadPoolExecutor
+        cores = max(1, min(len(os.sched_getaffinity(0)), 16, NH))
+        bounds = [NH * i // cores for i in range(cores + 1)]
+
+        def part(i):
+            for layout, direction in variants:
+                Hl, Sl = host[layout]
+                lo, hi = bounds[i], bounds[i + 1]
+                oracle.correct_h0(Hl[:, lo:hi], M[:, lo:hi], Sl[:, lo:hi], layout, direction)
+        with ThreadPoolExecutor(cores) as pool:
+            reps_mt, t0 = 0, time.perf_counter()
+            while True:
+                list(pool.map(part, range(cores)))
+                reps_mt += 1
+                if time.perf_counter() - t0 >= args.cpu_seconds / 2:
+                    break
+            el_mt = time.perf_counter() - t0
+        result["cpu_baseline_all_cores"] = {
+            "value": reps_mt * corrections_per_step / el_mt, "unit": "segment-state corrections/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"the full step repeated {reps_mt}x in {el_mt:.1f} s, heads split over {cores} threads",
         }
 
     if args.copy_calibration:
