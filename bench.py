@@ -259,8 +259,8 @@ def run_configs(args) -> int:
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on a "
-              "single MI355X: chains shard across GPUs with no exchange, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (one MI355X per "
+              "process; chains shard across GPUs with no exchange between them)", file=sys.stderr)
         return 2
 
     if args.sweep:
