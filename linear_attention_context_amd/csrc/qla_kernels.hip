@@ -100,9 +100,11 @@ constexpr int kTileV = 16;  // kv-view columns per workgroup
 #ifndef QLA_GROUPED_WAVES
 #define QLA_GROUPED_WAVES(K) ((K) >= 128 ? 8 : 4)
 #endif
-// Prefetch distance in units (panels) of M.
+// Prefetch distance in units (panels) of M.  Backward at K = 128 prefetches
+// one step ahead: with the L2 warm-up two steps ahead of that, a deeper
+// register ring measured slower.
 #ifndef QLA_PREFETCH_UNITS
-#define QLA_PREFETCH_UNITS(K, FWD) ((K) >= 256 ? 1 : (K) >= 128 ? ((FWD) ? 3 : 2) : 3)
+#define QLA_PREFETCH_UNITS(K, FWD) ((K) >= 256 ? 1 : (K) >= 128 ? ((FWD) ? 3 : 1) : 3)
 #endif
 
 template <int K, int WAVES_, bool FWD_>
