@@ -108,3 +108,24 @@ def test_empty_calls_touch_nothing():
         assert qla.raw_correct_h0(H, M, None, out, "kv", "fwd", batch, heads, n, 64, 64) == 0
     torch.cuda.synchronize()
     assert bool((out == 5.0).all())
+
+
+@pytest.mark.parametrize("K", [128, 256])
+def test_widest_state(K):
+    """V = 4096 (256 column tiles) at the larger head dims, both kernels' paths."""
+    V = 4096
+    H, M, S0 = qi.random_case(70 + K, (1, 1), 2, K, V)
+    for layout, direction in VARIANTS:
+        ref = oracle.correct_h0(lay(H, layout), M, lay(S0, layout), layout, direction)
+        got = run_hip(lay(H, layout), M, lay(S0, layout), layout, direction).cpu().numpy()
+        assert_parity(got, ref, f"K={K} V={V} {layout} {direction}")
+
+
+def test_many_chains():
+    """5000 chains of one 16-column tile: a grid far past one workgroup per CU,
+    not a multiple of the XCD count, checked on every state."""
+    H, M, S0 = qi.random_case(91, (5, 1000), 2, 64, 16)
+    for layout, direction in [("kv", "fwd"), ("vk", "bwd")]:
+        ref = oracle.correct_h0(lay(H, layout), M, lay(S0, layout), layout, direction)
+        got = run_hip(lay(H, layout), M, lay(S0, layout), layout, direction).cpu().numpy()
+        assert_parity(got, ref, f"5000 chains {layout} {direction}")
