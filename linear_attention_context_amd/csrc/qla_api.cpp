@@ -63,6 +63,9 @@ int check_buffers(const float* H, const float* M, const float* S0, const float* 
 {
     if (!H || !M || !out) return QLA_ERR_NULL;
     if (!aligned16(H) || !aligned16(M) || !aligned16(out) || (S0 && !aligned16(S0))) return QLA_ERR_ALIGN;
+    // Byte counts below must not wrap: 2^40 states of at most 4 MiB each stay
+    // within 64 bits (and far beyond any device's memory).
+    if (segments > (1LL << 40)) return QLA_ERR_SHAPE;
     const size_t state = (size_t)K * V * sizeof(float);
     const size_t hbytes = (size_t)segments * state;
     const size_t mbytes = (size_t)segments * K * K * sizeof(float);

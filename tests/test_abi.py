@@ -71,6 +71,11 @@ def test_shape_errors(lib, kw):
     assert call(**kw) == -3
 
 
+def test_size_overflow_rejected(lib):
+    """A call whose byte counts would wrap 64 bits is a shape error, not a launch."""
+    assert call(batch=2 ** 20, heads=2 ** 10, n_seg=2 ** 30, K=256, V=16) == -3
+
+
 def test_empty_calls_return_ok_without_pointers(lib):
     for kw in [dict(batch=0), dict(heads=0), dict(n_seg=0)]:
         assert call(H=None, M=None, out=None, **kw) == 0
