@@ -15,14 +15,15 @@ import ctypes
 import os
 
 __all__ = [
-    "QLA_LAYOUT_KV", "QLA_LAYOUT_VK", "QLA_DIR_FWD", "QLA_DIR_BWD", "QLA_MAX_GROUPS",
-    "QlaError", "qla_correct_h0", "qla_correct_h0_grouped", "qla_status_str",
-    "raw_correct_h0", "raw_correct_h0_grouped", "load_library", "library_path",
+    "QLA_LAYOUT_KV", "QLA_LAYOUT_VK", "QLA_DIR_FWD", "QLA_DIR_BWD", "QLA_MAX_GROUPS", "QLA_MAX_SEQS",
+    "QlaError", "qla_correct_h0", "qla_correct_h0_grouped", "qla_correct_h0_varlen", "qla_status_str",
+    "raw_correct_h0", "raw_correct_h0_grouped", "raw_correct_h0_varlen", "load_library", "library_path",
 ]
 
 QLA_LAYOUT_KV, QLA_LAYOUT_VK = 0, 1
 QLA_DIR_FWD, QLA_DIR_BWD = 0, 1
 QLA_MAX_GROUPS = 64
+QLA_MAX_SEQS = 256
 STATUS = {
     0: "QLA_OK", -1: "QLA_ERR_NULL", -2: "QLA_ERR_ENUM", -3: "QLA_ERR_SHAPE", -4: "QLA_ERR_ALIGN",
     -5: "QLA_ERR_ALIAS", -6: "QLA_ERR_GROUPS", -7: "QLA_ERR_LAUNCH", -8: "QLA_ERR_MEMORY",
@@ -160,8 +161,9 @@ def raw_correct_h0_varlen(H, M, S0, out, layout, direction, seg_offsets, heads, 
         arr, n = None, (0 if n_seqs is None else n_seqs)
     else:
         offs = [int(x) for x in seg_offsets]
-        arr = (ctypes.c_int * max(len(offs), 1))(*offs)
         n = len(offs) - 1 if n_seqs is None else n_seqs
+        # the library reads n + 1 offsets: never past the array (missing ones read as 0)
+        arr = (ctypes.c_int * max(len(offs), n + 1, 1))(*offs)
     return lib.qla_correct_h0_varlen(_ptr(H), _ptr(M), _ptr(S0), _ptr(out),
                                      _enum(layout, _LAYOUT_NAMES), _enum(direction, _DIR_NAMES),
                                      arr, n, heads, K, V, _stream(stream))
