@@ -851,7 +851,18 @@ struct FwdDma {
     }
 
     // ---- MFMA waves -------------------------------------------------------
-    template <int B>
+    // The step's global accesses go out between MFMA blocks late in the
+    // step: out of step s-1 before block kStoreAt, H of step s+HA before
+    // block kLoadAt.  Right after the barrier the producers fill the CU's
+    // vector memory queue, and an access waiting for a slot there holds up
+    // this wave; late in the step the queue has drained, and issuing them
+    // between blocks rather than all after the last one lets the other
+    // wave's MFMAs cover their issue.
+    static constexpr int kStoreAt = 5 * BP / 8, kLoadAt = 7 * BP / 8;
+    static_assert(0 < kStoreAt && kStoreAt < kLoadAt && kLoadAt < BP, "store and load points inside the step");
+
+    // MFMA blocks B .. E-1.
+    template <int B, int E = BP>
     static __device__ __forceinline__ void blocks(Ctx& X, const Lane& L)
     {
         constexpr int nr = B + MA < BP ? T : 0;
@@ -874,13 +885,13 @@ struct FwdDma {
         if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * T, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (B + 1 < BP) blocks<B + 1>(X, L);
+        if constexpr (B + 1 < E) blocks<B + 1, E>(X, L);
     }
 
     // Step s (LSX = s % HR selects the H register slot).  Barrier; operand
-    // reads (first staged M blocks, the other waves' state rows); out of step
-    // s-1 and H of step s+1 on the way; the MFMAs; P = Y + X(H_j) into the
-    // next state slot and the own-row registers.
+    // reads (first staged M blocks, the other waves' state rows); the MFMAs,
+    // with out of step s-1 and H of step s+HA issued between the last blocks;
+    // P = Y + X(H_j) into the next state slot and the own-row registers.
     template <int LSX>
     static __device__ __forceinline__ void step(int s, Ctx& X, const Chain& C, f4 (&h)[HR][T], float* lds,
                                                 const Lane& L)
@@ -906,13 +917,13 @@ struct FwdDma {
 #pragma unroll
         for (int t = 0; t < T; ++t) X.acc[t] = f4{0.f, 0.f, 0.f, 0.f};
         __builtin_amdgcn_sched_barrier(0);
-        blocks<0>(X, L);
-        // The wave's few global accesses go out once the step's MFMAs are
-        // issued: right after the barrier the producers fill the CU's vector
-        // memory queue, and a load or store waiting for a slot there would
-        // hold up this wave's MFMAs.
+        blocks<0, kStoreAt>(X, L);
         Tl::store_state(X.out_prev, X.own, L);
+        __builtin_amdgcn_sched_barrier(0);
+        blocks<kStoreAt, kLoadAt>(X, L);
         Tl::load_state(h[(LSX + HA) % HR], Hr, L);
+        __builtin_amdgcn_sched_barrier(0);
+        blocks<kLoadAt, BP>(X, L);
         if constexpr (QLA_M_TOUCH > 0) {
             asm volatile("" ::"v"(X.touched[LSX & 1]));
             X.touched[LSX & 1] = touch(C, s + QLA_M_TOUCH + 1, X, L);
