@@ -415,6 +415,10 @@ def main(argv=None):
         d = per_launch[v]
         per_call_us[f"{layout}_{direction}"] = {"mean": float(d.mean()), "median": float(np.median(d)),
                                                "min": float(d.min()), "max": float(d.max())}
+        if args.mode == "graph" and len(d) >= 75:
+            # the pages' statistic: 5 rounds of 15 replays, the median of the round medians
+            rounds = [np.median(d[r * 15:(r + 1) * 15]) for r in range(5)]
+            per_call_us[f"{layout}_{direction}"]["median_of_5_round_medians"] = float(np.median(rounds))
 
     corrections_per_step = nv * B * NH * N
     value = corrections_per_step / (ms_per_step * 1e-3)
