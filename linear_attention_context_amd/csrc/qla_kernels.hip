@@ -889,9 +889,10 @@ struct FwdDma {
     }
 
     // Step s (LSX = s % HR selects the H register slot).  Barrier; operand
-    // reads (first staged M blocks, the other waves' state rows); the MFMAs,
-    // with out of step s-1 and H of step s+HA issued between the last blocks;
-    // P = Y + X(H_j) into the next state slot and the own-row registers.
+    // reads (first staged M blocks, the other waves' state rows); the MFMAs
+    // accumulating onto X(H_j), with out of step s-1 and H of step s+HA
+    // issued between the last blocks; the new state into the next state slot
+    // and the own-row registers.
     template <int LSX>
     static __device__ __forceinline__ void step(int s, Ctx& X, const Chain& C, f4 (&h)[HR][T], float* lds,
                                                 const Lane& L)
@@ -914,8 +915,14 @@ struct FwdDma {
 #pragma unroll
             for (int t = 0; t < T; ++t) X.mo[b][t] = Tl::stage_read(X.st, t, b, L);
         Tl::template read_pv<0, kOwn, BP>(X.pv, X.cur, L);
+        // The accumulator starts at X(H_j) (loaded HA steps ago), so the new
+        // state is ready as soon as the last MFMA retires.
+        {
+            f4 hx[T];
+            Tl::frag_from_vecs(hx, h[LSX]);
 #pragma unroll
-        for (int t = 0; t < T; ++t) X.acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < T; ++t) X.acc[t] = hx[t];
+        }
         __builtin_amdgcn_sched_barrier(0);
         blocks<0, kStoreAt>(X, L);
         Tl::store_state(X.out_prev, X.own, L);
@@ -929,10 +936,6 @@ struct FwdDma {
             X.touched[LSX & 1] = touch(C, s + QLA_M_TOUCH + 1, X, L);
         }
 
-        f4 hx[T];
-        Tl::frag_from_vecs(hx, h[LSX]);
-#pragma unroll
-        for (int t = 0; t < T; ++t) X.acc[t] += hx[t];
         debug_delay(L.wave, s, 1);
         Tl::put_state(nxt, X.acc, L);
 #pragma unroll
