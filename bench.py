@@ -498,9 +498,15 @@ def main(argv=None):
             if time.perf_counter() - t0 >= args.cpu_seconds:
                 break
         el = time.perf_counter() - t0
+        cpu_model = ""
+        try:
+            with open("/proc/cpuinfo") as f:
+                cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+        except OSError:
+            pass
         result["cpu_baseline"] = {
             "value": reps * corrections_per_step / el, "unit": "segment-state corrections/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "host_cores_available": len(os.sched_getaffinity(0)),
             "sample": f"the full step (kv fwd + vk fwd, {corrections_per_step} corrections) repeated {reps}x "
                       f"in {el:.1f} s, fp64 plain loops, 1 thread",
         }
