@@ -213,6 +213,17 @@ def pin_layout_transpose(impl, seed=16):
         assert np.allclose(qi.to_vk(vk), kv, rtol=1e-13, atol=1e-13), d
 
 
+def pin_layout_transpose_square(impl, seed=20):
+    """As pin_layout_transpose with K = V and a non-symmetric S0: a vk path that
+    reads S0, H or out in the kv orientation (shapes alike) must still fail."""
+    H, M, S0 = qi.random_case(seed, (2,), 3, 5, 5)
+    assert not np.allclose(S0, np.swapaxes(S0, -1, -2))
+    for d in DIRECTIONS:
+        kv = impl(H, M, S0, "kv", d)
+        vk = impl(qi.to_vk(H), M, qi.to_vk(S0), "vk", d)
+        assert np.allclose(qi.to_vk(vk), kv, rtol=1e-13, atol=1e-13), d
+
+
 def pin_adjoint(impl, seed=17):
     """<fwd_M(X), Y> = <X, bwd_M'(Y)> with S0 = 0 and M'_j = M_{j+1} (M'_{n-1} arbitrary)."""
     n, K, V = 5, 7, 4
@@ -282,6 +293,6 @@ def pin_golden(impl):
 
 ALL_PINS = [
     pin_m_zero, pin_m_identity, pin_scalar_geometric, pin_diagonal,
-    pin_bruteforce_exact, pin_signed_permutation, pin_layout_transpose,
+    pin_bruteforce_exact, pin_signed_permutation, pin_layout_transpose, pin_layout_transpose_square,
     pin_adjoint, pin_reverse, pin_linearity, pin_coded_sentinel, pin_golden,
 ]

@@ -22,10 +22,14 @@ def _make(mutation=None):
         lead = H.shape[:-3]
         S = np.zeros(lead + H.shape[-2:]) if S0 is None else \
             _kvview(np.asarray(S0, np.float64), layout).copy()
+        if mutation == "vk_s0_untransposed" and layout == "vk" and S0 is not None and S.shape[-1] == S.shape[-2]:
+            S = np.asarray(S0, np.float64).copy()
         if mutation == "s0_ignored":
             S = np.zeros_like(S)
         out = np.empty_like(H)
         order = list(range(n)) if direction == "fwd" else list(range(n - 1, -1, -1))
+        if mutation == "skip_last" and n > 1:
+            order = order[:-1]
         if mutation == "bwd_forward_order" and direction == "bwd":
             order = list(range(n))
         for step, j in enumerate(order):
@@ -59,6 +63,10 @@ def _make(mutation=None):
             else:
                 out[..., j, :, :] = S_new
             S = S_new
+        if mutation == "skip_last" and n > 1:
+            out[..., order[-1] + (1 if direction == "fwd" else -1), :, :] = 0.0
+        if mutation == "vk_out_untransposed" and layout == "vk" and out.shape[-1] == out.shape[-2]:
+            return np.ascontiguousarray(out)
         return np.ascontiguousarray(_kvview(out, layout))
     return impl
 
@@ -66,7 +74,7 @@ def _make(mutation=None):
 MUTATIONS = [
     "drop_h", "minus_h", "bwd_no_transpose", "fwd_transposed", "bwd_forward_order",
     "m_index_shift", "h_index_shift", "s0_ignored", "s0_added", "vk_wrong_side",
-    "emit_previous",
+    "emit_previous", "vk_s0_untransposed", "vk_out_untransposed", "skip_last",
 ]
 
 
