@@ -37,6 +37,10 @@ def _make(mutation=None):
             Hj = H[..., j, :, :]
             if mutation == "h_index_shift" and direction == "fwd":
                 Hj = H[..., max(j - 1, 0), :, :]
+            if mutation == "h_index_shift_bwd" and direction == "bwd":
+                Hj = H[..., min(j + 1, n - 1), :, :]
+            if mutation == "chain_mix" and H.ndim >= 4 and H.shape[0] > 1:
+                Hj = np.roll(H[..., j, :, :], 1, axis=0)
             if mutation == "m_index_shift" and direction == "bwd":
                 if j + 1 < n:
                     Mj = M[..., j + 1, :, :]
@@ -74,7 +78,8 @@ def _make(mutation=None):
 MUTATIONS = [
     "drop_h", "minus_h", "bwd_no_transpose", "fwd_transposed", "bwd_forward_order",
     "m_index_shift", "h_index_shift", "s0_ignored", "s0_added", "vk_wrong_side",
-    "emit_previous", "vk_s0_untransposed", "vk_out_untransposed", "skip_last",
+    "emit_previous", "vk_s0_untransposed", "vk_out_untransposed", "skip_last", "h_index_shift_bwd",
+    "chain_mix",
 ]
 
 
