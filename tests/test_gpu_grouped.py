@@ -48,3 +48,19 @@ def test_grouped_uneven(K, with_s0):
             Sh = None if s0_flat is None else s0_flat[:, h].reshape(shape[:1] + shape[2:])
             ref = oracle.correct_h0(Hh, M[:, h], Sh, layout, direction)
             assert_parity(got[:, h].reshape(shape), ref, f"K={K} head {h} {layout} {direction}")
+
+
+def test_grouped_in_place():
+    """out == H for a grouped call: the same bits as a separate out buffer."""
+    import torch
+
+    import linear_attention_context_amd as qla
+    batch, heads, n, K = 1, 7, 4, 128
+    H_kv, M, S0_kv = qi.random_case(777, (batch, heads), n, K, K)
+    Hd, Md, Sd = to_device(H_kv), to_device(M), to_device(S0_kv)
+    sep = torch.full_like(Hd, float("nan"))
+    qla.qla_correct_h0_grouped(Hd, Md, Sd, sep, GROUPS, batch, heads, n, K, K)
+    torch.cuda.synchronize()
+    qla.qla_correct_h0_grouped(Hd, Md, Sd, Hd, GROUPS, batch, heads, n, K, K)
+    torch.cuda.synchronize()
+    assert torch.equal(Hd.view(torch.int32), sep.view(torch.int32))
