@@ -77,7 +77,7 @@ typedef unsigned u2 __attribute__((ext_vector_type(2)));
 #define QLA_DMA_WAVES 4
 #endif
 // Forward K <= 128: H is loaded this many steps ahead, and M_j's lines are
-// touched into L2 this many steps ahead of its copy (0: off).
+// warmed into L2 this many steps ahead of its copy (0: off).
 #ifndef QLA_H_AHEAD
 #define QLA_H_AHEAD 3
 #endif
@@ -762,7 +762,8 @@ struct Tile {
 // memory into one of two LDS stages with 16-byte LDS-DMA buffer loads (the
 // data never passes through registers; each producer issues an equal share
 // of the copies, so that enough of them are in flight to cover the memory
-// latency), wait for them, and join the step barrier.
+// latency), issue the L2 warm-up loads for later steps, wait for the copies,
+// and join the step barrier.
 // Waves 0 .. CW-1 compute as above, reading their rows of M from the stage;
 // they issue no M loads, so their instruction streams are MFMAs and LDS
 // reads.  One barrier per step orders everything: after the barrier that
@@ -785,7 +786,8 @@ struct FwdDma {
     static constexpr int kOwn = T;
     static constexpr int MA = 2;                      // staged reads run two blocks ahead
     static constexpr int STAGE = K * K;               // floats per M stage
-    static constexpr int LDS_FLOATS = S::STATE_FLOATS + 2 * STAGE;
+    static constexpr int WARM = S::STATE_FLOATS + 2 * STAGE;  // 64 floats the warm-up loads land in
+    static constexpr int LDS_FLOATS = WARM + 64;
     static constexpr int kDma = K * K / 256;          // 1 KiB copies per M
     static constexpr int HA = QLA_H_AHEAD;            // H is loaded HA steps ahead
     static constexpr int HR = HA + 1;                 // H register slots
@@ -797,27 +799,50 @@ struct FwdDma {
         f4 own[T];
         f4 pv[K / 16];
         f4 mo[MA + 1][T];
-        float touched[2];  // cache warm-up loads of the last two steps
         const float* cur;
         const float* st;
         __amdgpu_buffer_rsrc_t out_prev;
-        int tile, tiles;
     };
 
-    // L2 warm-up of M_j ahead of its copy.  The chain's workgroups sit on one
-    // XCD and copy the same M_j; together they touch each of its 128-byte
-    // lines once (one 4-byte load per line: MFMA wave w of tile t takes lines
-    // t + tiles*(w + CW*lane)), so the copy that follows hits in L2 instead of
-    // waiting on HBM.  The loaded value is consumed two steps later, when the
-    // wait the compiler places for it is long satisfied; lanes past the end
-    // use an out-of-range offset and touch nothing.
+    // L2 warm-up loads, issued by the producers right after each step's copy.
+    // A CU returns vector-memory data in issue order, so a load that misses
+    // to HBM holds up every load issued after it on that CU, the next copy of
+    // M included.  The data of step s+1 is therefore brought into L2 ahead of
+    // time by one 4-byte load per 128-byte line, each issued right behind a
+    // copy so that it has a whole step to return before the next copy goes
+    // out: the M_j lines (the chain's workgroups sit on one XCD and copy the
+    // same M_j, so together they load each line once: producer p of tile t
+    // takes lines t + tiles*(p + PW*lane)), and the lines of this tile's H_j
+    // one step before the MFMA waves load it.  The loaded words land in a
+    // 256-byte LDS area nothing reads; lanes past the end use an out-of-range
+    // offset and load nothing.
+    using lds_ptr = __attribute__((address_space(3))) void*;
     static constexpr int kLines = K * K * 4 / 128;
-    static __device__ __forceinline__ float touch(const Chain& C, int s, const Ctx& X, const Lane& L)
+    static __device__ __forceinline__ void warm_m(const Chain& C, float* sink, int s, int p, int tile, int tiles)
     {
-        const bool live = QLA_M_TOUCH > 0 && s < C.n_seg;
+        const bool live = s < C.n_seg;
         const __amdgpu_buffer_rsrc_t r = rsrc(C.M + (size_t)Tl::seg(C, live ? s : 0) * K * K, live ? kMatBytes : 0u);
-        const int line = X.tile + X.tiles * (L.wave + CW * (int)(threadIdx.x & 63));
-        return bload1(r, line < kLines ? 128u * (unsigned)line : kOutOfRange);
+        const int line = tile + tiles * (p + PW * (int)(threadIdx.x & 63));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)sink, 4, line < kLines ? 128 * line : (int)kOutOfRange,
+                                                 0, 0, 0);
+    }
+    // kv: one word in each row's 64-byte piece of the tile (rows p + PW*lane);
+    // vk: one word in each 128-byte line of the tile's rows.
+    static __device__ __forceinline__ void warm_h(const Chain& C, float* sink, int s, int p, int tile, int V)
+    {
+        const bool live = s < C.n_seg;
+        const unsigned bytes = (unsigned)K * V * 4u;
+        const __amdgpu_buffer_rsrc_t r = rsrc(C.H + (size_t)Tl::seg(C, live ? s : 0) * (bytes / 4), live ? bytes : 0u);
+        const int idx = p + PW * (int)(threadIdx.x & 63);
+        unsigned off = kOutOfRange;
+        if constexpr (LAYOUT == QLA_LAYOUT_KV) {
+            if (idx < K) off = 4u * (unsigned)(idx * V) + 64u * (unsigned)tile;
+        } else {
+            constexpr int kRowLines = K * 4 / 128;
+            const int i = idx / kRowLines, c = idx % kRowLines, row = kTileV * tile + i;
+            if (i < kTileV && row < V) off = 4u * (unsigned)(row * K) + 128u * (unsigned)c;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)sink, 4, (int)off, 0, 0, 0);
     }
 
     // ---- producer ---------------------------------------------------------
@@ -839,21 +864,34 @@ struct FwdDma {
         }
     }
 
-    static __device__ __forceinline__ void producer(const Chain& C, float* lds, int p)
+    // Each step: the copy, then the warm-ups for M_{s+1+QLA_M_TOUCH} and for
+    // the H the MFMA waves load next step; the barrier waits for the copy
+    // only (vmcnt counts in issue order, so leaving the warm-ups outstanding
+    // still covers every copy instruction).
+    static constexpr int kWarmPerStep = (QLA_M_TOUCH > 0) + 1;
+    static __device__ __forceinline__ void producer(const Chain& C, float* lds, int p, int tile, int V)
     {
         float* stages = lds + S::STATE_FLOATS;
+        float* sink = lds + WARM;
+        const int tiles = (V + kTileV - 1) / kTileV;
         dma_unit(C.M + (size_t)Tl::seg(C, 0) * K * K, stages, p);
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int u = 1; u <= QLA_M_TOUCH; ++u) warm_m(C, sink, u, p, tile, tiles);
+        warm_h(C, sink, HA, p, tile, V);
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(QLA_M_TOUCH + 1) : "memory");
         for (int s = 0; s + 1 < C.n_seg; ++s) {
             dma_unit(C.M + (size_t)Tl::seg(C, s + 1) * K * K, stages + ((s + 1) & 1) * STAGE, p);
-            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+            if constexpr (QLA_M_TOUCH > 0) warm_m(C, sink, s + 1 + QLA_M_TOUCH, p, tile, tiles);
+            warm_h(C, sink, s + 1 + HA, p, tile, V);
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWarmPerStep) : "memory");
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
     // ---- MFMA waves -------------------------------------------------------
     // The step's global accesses go out between MFMA blocks late in the
-    // step: out of step s-1 before block kStoreAt, H of step s+HA before
-    // block kLoadAt.  Right after the barrier the producers fill the CU's
+    // step: out of step s-1 before block kStoreAt, H of step s+HA (already
+    // warmed into L2 by the producers) before block kLoadAt.  Right after the barrier the producers fill the CU's
     // vector memory queue, and an access waiting for a slot there holds up
     // this wave; late in the step the queue has drained, and issuing them
     // between blocks rather than all after the last one lets the other
@@ -931,10 +969,6 @@ struct FwdDma {
         Tl::load_state(h[(LSX + HA) % HR], Hr, L);
         __builtin_amdgcn_sched_barrier(0);
         blocks<kLoadAt, BP>(X, L);
-        if constexpr (QLA_M_TOUCH > 0) {
-            asm volatile("" ::"v"(X.touched[LSX & 1]));
-            X.touched[LSX & 1] = touch(C, s + QLA_M_TOUCH + 1, X, L);
-        }
 
         debug_delay(L.wave, s, 1);
         Tl::put_state(nxt, X.acc, L);
@@ -959,8 +993,6 @@ struct FwdDma {
     {
         const Lane L = Tl::make_lane(tile * kTileV, V);
         Ctx X;
-        X.tile = tile;
-        X.tiles = (V + kTileV - 1) / kTileV;
         f4 h[HR][T];
         f4 sv[T];
         Tl::load_state(sv, rsrc(S0c ? S0c : C.H, S0c ? L.state_bytes : 0u), L);
@@ -972,9 +1004,6 @@ struct FwdDma {
         }
         Tl::frag_from_vecs(X.own, sv);
         Tl::put_state(lds, X.own, L);
-        // Warm-up of the units whose copies come before the steps' own touches.
-        X.touched[0] = QLA_M_TOUCH > 1 ? touch(C, 2, X, L) : 0.f;
-        X.touched[1] = QLA_M_TOUCH > 0 ? touch(C, 1, X, L) : 0.f;
         int s = 0;
         for (; s + HR <= C.n_seg; s += HR) {
             step<0>(s, X, C, h, lds, L);
@@ -1002,7 +1031,7 @@ struct FwdDma {
         // A chain without segments: every wave leaves before any barrier.
         if (__builtin_amdgcn_readfirstlane(C.n_seg) <= 0) return;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        if (wave >= CW) producer(C, lds, wave - CW);
+        if (wave >= CW) producer(C, lds, wave - CW, tile, V);
         else consumer(C, S0c, lds, tile, V);
     }
 };
