@@ -868,6 +868,14 @@ struct FwdDma {
     // the H the MFMA waves load next step; the barrier waits for the copy
     // only (vmcnt counts in issue order, so leaving the warm-ups outstanding
     // still covers every copy instruction).
+    // The wait is correct only if the warm-ups are issued after every copy:
+    // a compiler barrier keeps both the IR passes and the machine scheduler
+    // from moving them across (tests/test_kernel_isa.py checks the built code).
+    static __device__ __forceinline__ void copies_before_warmups()
+    {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
     static constexpr int kWarmPerStep = (QLA_M_TOUCH > 0) + 1;
     static __device__ __forceinline__ void producer(const Chain& C, float* lds, int p, int tile, int V)
     {
@@ -875,12 +883,14 @@ struct FwdDma {
         float* sink = lds + WARM;
         const int tiles = (V + kTileV - 1) / kTileV;
         dma_unit(C.M + (size_t)Tl::seg(C, 0) * K * K, stages, p);
+        copies_before_warmups();
 #pragma unroll
         for (int u = 1; u <= QLA_M_TOUCH; ++u) warm_m(C, sink, u, p, tile, tiles);
         warm_h(C, sink, HA, p, tile, V);
         asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(QLA_M_TOUCH + 1) : "memory");
         for (int s = 0; s + 1 < C.n_seg; ++s) {
             dma_unit(C.M + (size_t)Tl::seg(C, s + 1) * K * K, stages + ((s + 1) & 1) * STAGE, p);
+            copies_before_warmups();
             if constexpr (QLA_M_TOUCH > 0) warm_m(C, sink, s + 1 + QLA_M_TOUCH, p, tile, tiles);
             warm_h(C, sink, s + 1 + HA, p, tile, V);
             asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWarmPerStep) : "memory");
