@@ -11,8 +11,8 @@ of their own, 16 x 52.4 MB = 839 MB > the 256 MB MALL, so every call streams
 its inputs from HBM.  The same calls on one resident set (warm) and the
 bandwidth of a plain 1 GiB device copy are reported beside it.
 
-Timing: --warmup untimed steps first (320 by default: per-call times keep
-falling for the first couple of hundred calls of a process), then the steps'
+Timing: --warmup untimed steps first (640 by default: per-call times keep
+falling for the first thousand or so calls of a process, about 20 ms), then the steps'
 kv calls back to back, then their vk calls, with HIP events on the launch
 stream at the boundaries (--mode direct, default).
 --mode graph follows the pages' protocol instead: each variant's launches are
@@ -56,7 +56,7 @@ def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=320)
-    p.add_argument("--warmup", type=int, default=320)
+    p.add_argument("--warmup", type=int, default=640)
     p.add_argument("--mode", choices=("direct", "graph"), default="direct",
                    help="direct launches (default) or replays of captured hipGraphs")
     p.add_argument("--graph-calls", type=int, default=16, help="launches per captured graph (--mode graph)")
@@ -143,6 +143,7 @@ def run_sweep(args) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    settle = True
     K = V = 128
     copy_gbps = measured_copy_gbps(torch, dev)
     for tokens in qi.SWEEP_TOKENS:
@@ -164,8 +165,11 @@ def run_sweep(args) -> int:
                                                direction, 1, heads, n, K, V, stream=stream.cuda_stream)
                         times = {}
                         for label, order in (("warm", [0] * 64), ("rotated", [i % rot for i in range(max(64, rot))])):
-                            for i in range(64):  # untimed: per-call times settle over the first calls
+                            # untimed; the first point also lets the per-call times of the
+                            # process settle (about a thousand calls)
+                            for i in range(1024 if settle else 64):
                                 call(sets[order[i % len(order)]])
+                            settle = False
                             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                             e0.record(stream)
                             for i in order:
@@ -233,9 +237,9 @@ def run_configs(args) -> int:
                     qla.qla_correct_h0(x["H"], x["M"], x["S0"], x["out"], what[0], what[1], B, NH, N, K, V,
                                        stream=stream.cuda_stream)
             reps = 64 if nbytes < (64 << 20) else 8
-            # untimed calls first, a few milliseconds' worth: per-call times
-            # settle only after a couple of hundred short calls
-            n_warm = 256 if nbytes < (64 << 20) else 8
+            # untimed calls first: per-call times settle only after the first
+            # thousand or so short calls of a process (about 20 ms)
+            n_warm = 1024 if nbytes < (64 << 20) else 8
             times = {}
             for kind, order in (("warm", [0] * reps), ("rotated", [i % rot for i in range(max(reps, rot))])):
                 for i in range(n_warm):
