@@ -28,7 +28,7 @@
 // no wave reaches before its writes landed.  Read-before-reuse holds by
 // construction.
 //
-// Staging of M.  Forward at K <= 128 (FwdDma), dedicated producer waves copy
+// Staging of M.  At K <= 128 (DmaChain, both directions), dedicated producer waves copy
 // each M_j into one of two LDS stages, released by that same per-step barrier
 // (the pages' Hopper kernel also had a producer, with its own two-slot
 // buffers and hand-off; the slot-reuse race the note diagnoses, section
@@ -72,6 +72,9 @@ typedef unsigned u2 __attribute__((ext_vector_type(2)));
 #endif
 #ifndef QLA_FWD_DMA
 #define QLA_FWD_DMA 1
+#endif
+#ifndef QLA_BWD_DMA
+#define QLA_BWD_DMA 1
 #endif
 #ifndef QLA_DMA_WAVES
 #define QLA_DMA_WAVES 4
@@ -757,30 +760,55 @@ struct Tile {
     }
 };
 
-// Forward, K <= 128: producer waves and MFMA waves.  Waves CW .. CW+PW-1 of
+// K <= 128, both directions: producer waves and MFMA waves.  Waves CW .. CW+PW-1 of
 // the workgroup only move M: together they copy each M_j whole from global
 // memory into one of two LDS stages with 16-byte LDS-DMA buffer loads (the
 // data never passes through registers; each producer issues an equal share
 // of the copies, so that enough of them are in flight to cover the memory
 // latency), issue the L2 warm-up loads for later steps, wait for the copies,
 // and join the step barrier.
-// Waves 0 .. CW-1 compute as above, reading their rows of M from the stage;
-// they issue no M loads, so their instruction streams are MFMAs and LDS
-// reads.  One barrier per step orders everything: after the barrier that
+// Waves 0 .. CW-1 compute as above, reading their operand of M from the
+// stage: forward their rows of M (one 16-byte read per 16-k block), backward
+// the same columns of M, which are the rows of M^T (four 4-byte reads per
+// block; the copy cannot transpose).  They issue no M loads, so their
+// instruction streams are MFMAs and LDS reads.  One barrier per step orders everything: after the barrier that
 // opens step s the producer refills the stage of unit s-1 with unit s+1
 // (every MFMA wave finished reading it before arriving), and unit s+1 has
 // landed before the producer arrives at the barrier that opens step s+1.
 // The stage holds M row-major with each row's 16-byte chunks XOR-swizzled
 // by the row's low four bits, so the whole-row copy and the MFMA-layout
-// reads are both free of bank conflicts.
-template <int K, int LAYOUT>
-struct FwdDma {
+// reads of either direction are free of bank conflicts (backward, the four
+// rows a read instruction touches differ in bits 2-3 of k, which moves their
+// chunks to distinct banks).
+template <int K, int LAYOUT, int DIR = QLA_DIR_FWD>
+struct DmaChain {
     static constexpr int CW = QLA_WAVES(K, true);
     static constexpr int PW = QLA_DMA_WAVES;           // producer waves
     using Tl = Tile<K, LAYOUT, QLA_DIR_FWD, CW>;
     using S = typename Tl::S;
     using Lane = typename Tl::Lane;
     using Chain = typename Tl::Chain;
+    // Segment of step s: forward in order, backward in reverse.
+    static __device__ __forceinline__ int sg(const Chain& C, int s) { return DIR == QLA_DIR_FWD ? s : C.n_seg - 1 - s; }
+    // Staged operand of (t, block b): forward M[a0 + 16t + c][k] (the wave's
+    // rows, one 16-byte read); backward M[k][a0 + 16t + c] (a column, four
+    // 4-byte reads), k = 16 kb + 4g + q.
+    static __device__ __forceinline__ f4 rd(const float* st, int t, int b, const Lane& L, const int (&X_tofs)[4])
+    {
+        if constexpr (DIR == QLA_DIR_FWD) {
+            return Tl::stage_read(st, t, b, L);
+        } else {
+            // k & 15 = 4g + q does not depend on the block, so the lane's four
+            // byte offsets (tofs) are fixed; the block adds a uniform 16 K-float step.
+            static_assert(T == 1, "one row tile per wave");
+            const int kofs = __builtin_amdgcn_readfirstlane(((b + L.brot) & (BP - 1)) * 16 * K * 4);
+            const char* sb = reinterpret_cast<const char*>(st) + kofs;
+            f4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const float*>(sb + X_tofs[q]);
+            return v;
+        }
+    }
     static constexpr int T = S::T, BP = S::BP, LS = S::LS;
     static_assert(S::NP == 1, "one panel per step");
     static constexpr int kOwn = T;
@@ -802,6 +830,7 @@ struct FwdDma {
         const float* cur;
         const float* st;
         __amdgpu_buffer_rsrc_t out_prev;
+        int tofs[4];  // backward: byte offsets of the lane's staged column reads
     };
 
     // L2 warm-up loads, issued by the producers right after each step's copy.
@@ -821,7 +850,7 @@ struct FwdDma {
     static __device__ __forceinline__ void warm_m(const Chain& C, float* sink, int s, int p, int tile, int tiles)
     {
         const bool live = s < C.n_seg;
-        const __amdgpu_buffer_rsrc_t r = rsrc(C.M + (size_t)Tl::seg(C, live ? s : 0) * K * K, live ? kMatBytes : 0u);
+        const __amdgpu_buffer_rsrc_t r = rsrc(C.M + (size_t)sg(C, live ? s : 0) * K * K, live ? kMatBytes : 0u);
         const int line = tile + tiles * (p + PW * (int)(threadIdx.x & 63));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)sink, 4, line < kLines ? 128 * line : (int)kOutOfRange,
                                                  0, 0, 0);
@@ -832,7 +861,7 @@ struct FwdDma {
     {
         const bool live = s < C.n_seg;
         const unsigned bytes = (unsigned)K * V * 4u;
-        const __amdgpu_buffer_rsrc_t r = rsrc(C.H + (size_t)Tl::seg(C, live ? s : 0) * (bytes / 4), live ? bytes : 0u);
+        const __amdgpu_buffer_rsrc_t r = rsrc(C.H + (size_t)sg(C, live ? s : 0) * (bytes / 4), live ? bytes : 0u);
         const int idx = p + PW * (int)(threadIdx.x & 63);
         unsigned off = kOutOfRange;
         if constexpr (LAYOUT == QLA_LAYOUT_KV) {
@@ -882,14 +911,14 @@ struct FwdDma {
         float* stages = lds + S::STATE_FLOATS;
         float* sink = lds + WARM;
         const int tiles = (V + kTileV - 1) / kTileV;
-        dma_unit(C.M + (size_t)Tl::seg(C, 0) * K * K, stages, p);
+        dma_unit(C.M + (size_t)sg(C, 0) * K * K, stages, p);
         copies_before_warmups();
 #pragma unroll
         for (int u = 1; u <= QLA_M_TOUCH; ++u) warm_m(C, sink, u, p, tile, tiles);
         warm_h(C, sink, HA, p, tile, V);
         asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(QLA_M_TOUCH + 1) : "memory");
         for (int s = 0; s + 1 < C.n_seg; ++s) {
-            dma_unit(C.M + (size_t)Tl::seg(C, s + 1) * K * K, stages + ((s + 1) & 1) * STAGE, p);
+            dma_unit(C.M + (size_t)sg(C, s + 1) * K * K, stages + ((s + 1) & 1) * STAGE, p);
             copies_before_warmups();
             if constexpr (QLA_M_TOUCH > 0) warm_m(C, sink, s + 1 + QLA_M_TOUCH, p, tile, tiles);
             warm_h(C, sink, s + 1 + HA, p, tile, V);
@@ -925,7 +954,7 @@ struct FwdDma {
         mfma(1);
         if constexpr (nr > 0) {
 #pragma unroll
-            for (int t = 0; t < T; ++t) X.mo[(B + MA) % (MA + 1)][t] = Tl::stage_read(X.st, t, B + MA, L);
+            for (int t = 0; t < T; ++t) X.mo[(B + MA) % (MA + 1)][t] = rd(X.st, t, B + MA, L, X.tofs);
         }
         mfma(2);
         mfma(3);
@@ -947,21 +976,21 @@ struct FwdDma {
     {
         s = __builtin_amdgcn_readfirstlane(s);  // uniform: keeps the step's descriptors scalar
         float* nxt = lds + ((s + 1) & 1) * (kTileV * LS);
-        const int jp = s > 0 ? Tl::seg(C, s - 1) : 0;
+        const int jp = s > 0 ? sg(C, s - 1) : 0;
         X.out_prev = rsrc(C.out + (size_t)jp * (L.state_bytes / 4), s > 0 ? L.state_bytes : 0u);
         const bool live = s + HA < C.n_seg;
         const __amdgpu_buffer_rsrc_t Hr =
-            rsrc(C.H + (size_t)(live ? Tl::seg(C, s + HA) : 0) * (L.state_bytes / 4), live ? L.state_bytes : 0u);
+            rsrc(C.H + (size_t)(live ? sg(C, s + HA) : 0) * (L.state_bytes / 4), live ? L.state_bytes : 0u);
 
         __builtin_amdgcn_sched_barrier(0);
         lds_handoff();
         debug_delay(L.wave, s, 0);
         X.cur = lds + (s & 1) * (kTileV * LS);
-        X.st = lds + S::STATE_FLOATS + (s & 1) * STAGE + L.a0 * K;
+        X.st = lds + S::STATE_FLOATS + (s & 1) * STAGE + (DIR == QLA_DIR_FWD ? L.a0 * K : 0);
 #pragma unroll
         for (int b = 0; b < MA; ++b)
 #pragma unroll
-            for (int t = 0; t < T; ++t) X.mo[b][t] = Tl::stage_read(X.st, t, b, L);
+            for (int t = 0; t < T; ++t) X.mo[b][t] = rd(X.st, t, b, L, X.tofs);
         Tl::template read_pv<0, kOwn, BP>(X.pv, X.cur, L);
         // The accumulator starts at X(H_j) (loaded HA steps ago), so the new
         // state is ready as soon as the last MFMA retires.
@@ -1003,13 +1032,24 @@ struct FwdDma {
     {
         const Lane L = Tl::make_lane(tile * kTileV, V);
         Ctx X;
+        if constexpr (DIR != QLA_DIR_FWD) {
+            const int col = L.a0 + L.c;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = 4 * L.g + q;
+                X.tofs[q] = 4 * (r * K + 4 * ((col >> 2) ^ r) + (col & 3));
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) X.tofs[q] = 0;
+        }
         f4 h[HR][T];
         f4 sv[T];
         Tl::load_state(sv, rsrc(S0c ? S0c : C.H, S0c ? L.state_bytes : 0u), L);
 #pragma unroll
         for (int i = 0; i < HA; ++i) {
             const bool live = i < C.n_seg;
-            Tl::load_state(h[i], rsrc(C.H + (size_t)Tl::seg(C, live ? i : 0) * (L.state_bytes / 4),
+            Tl::load_state(h[i], rsrc(C.H + (size_t)sg(C, live ? i : 0) * (L.state_bytes / 4),
                                       live ? L.state_bytes : 0u), L);
         }
         Tl::frag_from_vecs(X.own, sv);
@@ -1023,7 +1063,7 @@ struct FwdDma {
             if constexpr (HR > 4) step<4 % HR>(s + 4, X, C, h, lds, L);
         }
         tail<0>(s, X, C, h, lds, L);
-        Tl::store_state(rsrc(C.out + (size_t)Tl::seg(C, C.n_seg - 1) * (L.state_bytes / 4), L.state_bytes), X.own,
+        Tl::store_state(rsrc(C.out + (size_t)sg(C, C.n_seg - 1) * (L.state_bytes / 4), L.state_bytes), X.own,
                         L);
     }
 
@@ -1078,7 +1118,19 @@ template <int K, int LAYOUT>
 __global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void correct_h0_fwd_dma_kernel(
     const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles)
 {
-    using D = FwdDma<K, LAYOUT>;
+    using D = DmaChain<K, LAYOUT>;
+    __shared__ __attribute__((aligned(16))) float lds[D::LDS_FLOATS];
+    const int id = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int chain = id / tiles;
+    const int tile = id - chain * tiles;
+    D::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds);
+}
+
+template <int K, int LAYOUT>
+__global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void correct_h0_bwd_dma_kernel(
+    const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles)
+{
+    using D = DmaChain<K, LAYOUT, QLA_DIR_BWD>;
     __shared__ __attribute__((aligned(16))) float lds[D::LDS_FLOATS];
     const int id = xcd_logical_id(blockIdx.x, gridDim.x);
     const int chain = id / tiles;
@@ -1120,7 +1172,21 @@ __global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void cor
     const float* H, const float* __restrict__ M, const float* S0, float* out, int heads, int V, int tiles,
     SeqTable seqs)
 {
-    using D = FwdDma<K, LAYOUT>;
+    using D = DmaChain<K, LAYOUT>;
+    __shared__ __attribute__((aligned(16))) float lds[D::LDS_FLOATS];
+    const int id = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int chain = id / tiles;
+    const int tile = id - chain * tiles;
+    const auto C = varlen_chain<typename D::Chain, K>(H, M, out, heads, V, chain, seqs);
+    D::run_chain(C, S0 ? S0 + (size_t)chain * K * V : nullptr, V, tile, lds);
+}
+
+template <int K, int LAYOUT>
+__global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void correct_h0_bwd_dma_varlen_kernel(
+    const float* H, const float* __restrict__ M, const float* S0, float* out, int heads, int V, int tiles,
+    SeqTable seqs)
+{
+    using D = DmaChain<K, LAYOUT, QLA_DIR_BWD>;
     __shared__ __attribute__((aligned(16))) float lds[D::LDS_FLOATS];
     const int id = xcd_logical_id(blockIdx.x, gridDim.x);
     const int chain = id / tiles;
@@ -1161,6 +1227,9 @@ hipError_t launch_one(const LaunchArgs& a)
     if constexpr (QLA_FWD_DMA && DIR == QLA_DIR_FWD && K <= 128) {
         hipLaunchKernelGGL((correct_h0_fwd_dma_kernel<K, LAYOUT>), grid, dim3(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)),
                            0, (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles);
+    } else if constexpr (QLA_BWD_DMA && DIR == QLA_DIR_BWD && K <= 128) {
+        hipLaunchKernelGGL((correct_h0_bwd_dma_kernel<K, LAYOUT>), grid, dim3(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)),
+                           0, (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles);
     } else {
         hipLaunchKernelGGL((correct_h0_kernel<K, LAYOUT, DIR>), grid, dim3(64 * Plain<K, LAYOUT, DIR>::WAVES), 0,
                            (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles);
@@ -1185,6 +1254,10 @@ hipError_t launch_varlen_one(const LaunchArgs& a, const SeqTable& seqs)
     const dim3 grid((unsigned)(a.chains * tiles));
     if constexpr (QLA_FWD_DMA && DIR == QLA_DIR_FWD && K <= 128) {
         hipLaunchKernelGGL((correct_h0_fwd_dma_varlen_kernel<K, LAYOUT>), grid,
+                           dim3(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)), 0, (hipStream_t)a.stream, a.H, a.M, a.S0,
+                           a.out, a.heads, a.V, tiles, seqs);
+    } else if constexpr (QLA_BWD_DMA && DIR == QLA_DIR_BWD && K <= 128) {
+        hipLaunchKernelGGL((correct_h0_bwd_dma_varlen_kernel<K, LAYOUT>), grid,
                            dim3(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)), 0, (hipStream_t)a.stream, a.H, a.M, a.S0,
                            a.out, a.heads, a.V, tiles, seqs);
     } else {

@@ -1,6 +1,6 @@
-"""Machine-code check of the forward producers' step barriers (CPU only).
+"""Machine-code check of the producer kernels' step barriers (CPU only).
 
-The producer waves of the forward kernel copy M_{s+1} into LDS with 16-byte
+The producer waves of the K <= 128 kernels (both directions) copy M_{s+1} into LDS with 16-byte
 LDS-DMA loads and then issue 4-byte LDS-DMA L2 warm-up loads for later steps.
 At the step barrier they wait with ``s_waitcnt vmcnt(N)``, N being the number
 of warm-ups just issued, and leave those outstanding.  Vector-memory counts
@@ -9,8 +9,8 @@ newest -- which is correct only if the N newest vector-memory instructions
 before the barrier are warm-ups and no copy of M comes after them.  The
 compiler schedules the code, so this test reads the machine code of the built
 libraries (the gfx950 code object inside each .so, disassembled with ROCm's
-llvm-objdump) and checks the order at every such barrier of every forward
-producer kernel.
+llvm-objdump) and checks the order at every such barrier of every producer
+kernel.
 """
 from __future__ import annotations
 
@@ -52,14 +52,14 @@ def _disassemble(lib: str, tmp_path) -> str:
 
 
 def _kernels(text: str):
-    """(symbol, instruction list) of every forward producer kernel."""
+    """(symbol, instruction list) of every producer kernel."""
     cur, body = None, []
     for raw in text.splitlines():
         m = re.match(r"^[0-9a-f]+ <(\S+)>:$", raw)
         if m:
             if cur is not None:
                 yield cur, body
-            cur, body = (m.group(1), []) if "correct_h0_fwd_dma" in m.group(1) else (None, [])
+            cur, body = (m.group(1), []) if re.search(r"correct_h0_(fwd|bwd)_dma", m.group(1)) else (None, [])
             continue
         if cur is not None:
             ins = raw.split("//")[0].strip()
@@ -101,8 +101,8 @@ def test_producer_barriers_cover_every_copy(name, tmp_path):
     if not os.path.exists(lib):
         pytest.skip(f"{name} is not built")
     kernels = list(_kernels(_disassemble(lib, tmp_path)))
-    # K in {64, 128} x {kv, vk}, plain and variable-length
-    assert len(kernels) == 8, [k for k, _ in kernels]
+    # {fwd, bwd} x K in {64, 128} x {kv, vk}, plain and variable-length
+    assert len(kernels) == 16, [k for k, _ in kernels]
     for sym, body in kernels:
         checked, problems = _check(body)
         # the barrier after the first copy and the one in the step loop, at least
