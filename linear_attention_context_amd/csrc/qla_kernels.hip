@@ -1195,15 +1195,43 @@ __global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void cor
     D::run_chain(C, S0 ? S0 + (size_t)chain * K * V : nullptr, V, tile, lds);
 }
 
+// One grouped launch: each workgroup looks up its head's (layout, direction)
+// and runs that variant.  At K <= 128 the variants are the producer kernel's
+// (every variant has the same block shape and LDS size there); at K = 256
+// the general kernel's, with one wave count for all four.
 template <int K>
-__global__ __launch_bounds__(64 * QLA_GROUPED_WAVES(K)) void correct_h0_grouped_kernel(
+struct Grouped {
+    static constexpr bool kDma = QLA_FWD_DMA && QLA_BWD_DMA && K <= 128;
+    static constexpr int WAVES = kDma ? QLA_WAVES(K, true) + QLA_DMA_WAVES : QLA_GROUPED_WAVES(K);
+    static constexpr int W = QLA_GROUPED_WAVES(K);
+    static constexpr int max2(int a, int b) { return a > b ? a : b; }
+    static constexpr int lds_floats()
+    {
+        if constexpr (kDma)
+            return max2(max2(DmaChain<K, QLA_LAYOUT_KV, QLA_DIR_FWD>::LDS_FLOATS,
+                             DmaChain<K, QLA_LAYOUT_KV, QLA_DIR_BWD>::LDS_FLOATS),
+                        max2(DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_FWD>::LDS_FLOATS,
+                             DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_BWD>::LDS_FLOATS));
+        else
+            return max2(Tile<K, QLA_LAYOUT_KV, QLA_DIR_FWD, W>::LDS_FLOATS, Tile<K, QLA_LAYOUT_KV, QLA_DIR_BWD, W>::LDS_FLOATS);
+    }
+    static constexpr int LDS_FLOATS = lds_floats();
+    template <int LAYOUT, int DIR>
+    static __device__ __forceinline__ void run(const float* H, const float* M, const float* S0, float* out, int n_seg,
+                                               int V, size_t chain, int tile, float* lds)
+    {
+        if constexpr (kDma) DmaChain<K, LAYOUT, DIR>::run(H, M, S0, out, n_seg, V, chain, tile, lds);
+        else Tile<K, LAYOUT, DIR, W>::run(H, M, S0, out, n_seg, V, chain, tile, lds);
+    }
+};
+
+template <int K>
+__global__ __launch_bounds__(64 * Grouped<K>::WAVES) void correct_h0_grouped_kernel(
     const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles, int heads,
     GroupTable table)
 {
-    constexpr int W = QLA_GROUPED_WAVES(K);
-    constexpr int F1 = Tile<K, QLA_LAYOUT_KV, QLA_DIR_FWD, W>::LDS_FLOATS;
-    constexpr int F2 = Tile<K, QLA_LAYOUT_KV, QLA_DIR_BWD, W>::LDS_FLOATS;
-    __shared__ __attribute__((aligned(16))) float lds[F1 > F2 ? F1 : F2];
+    using G = Grouped<K>;
+    __shared__ __attribute__((aligned(16))) float lds[G::LDS_FLOATS];
     const int id = xcd_logical_id(blockIdx.x, gridDim.x);
     const int chain = id / tiles;
     const int tile = id - chain * tiles;
@@ -1212,10 +1240,10 @@ __global__ __launch_bounds__(64 * QLA_GROUPED_WAVES(K)) void correct_h0_grouped_
     for (int i = 0; i < table.n; ++i)
         if (head >= table.begin[i] && head < table.begin[i] + table.count[i]) variant = table.variant[i];
     switch (variant) {
-    case 0: Tile<K, QLA_LAYOUT_KV, QLA_DIR_FWD, W>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
-    case 1: Tile<K, QLA_LAYOUT_KV, QLA_DIR_BWD, W>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
-    case 2: Tile<K, QLA_LAYOUT_VK, QLA_DIR_FWD, W>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
-    default: Tile<K, QLA_LAYOUT_VK, QLA_DIR_BWD, W>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
+    case 0: G::template run<QLA_LAYOUT_KV, QLA_DIR_FWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
+    case 1: G::template run<QLA_LAYOUT_KV, QLA_DIR_BWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
+    case 2: G::template run<QLA_LAYOUT_VK, QLA_DIR_FWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
+    default: G::template run<QLA_LAYOUT_VK, QLA_DIR_BWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
     }
 }
 
@@ -1282,7 +1310,7 @@ hipError_t launch_grouped_k(const LaunchArgs& a, const GroupTable& table)
 {
     const int tiles = (a.V + kTileV - 1) / kTileV;
     const dim3 grid((unsigned)(a.chains * tiles));
-    hipLaunchKernelGGL((correct_h0_grouped_kernel<K>), grid, dim3(64 * QLA_GROUPED_WAVES(K)), 0, (hipStream_t)a.stream,
+    hipLaunchKernelGGL((correct_h0_grouped_kernel<K>), grid, dim3(64 * Grouped<K>::WAVES), 0, (hipStream_t)a.stream,
                        a.H, a.M,
                        a.S0, a.out, a.n_seg, a.V, tiles, a.heads, table);
     return hipGetLastError();

@@ -30,6 +30,9 @@ TARGET = "hipv4-amdgcn-amd-amdhsa--gfx950"
 COPY = re.compile(r"^buffer_load_dwordx4\b.*\blds\b")
 WARM = re.compile(r"^buffer_load_dword\s.*\blds\b")
 VMEM = re.compile(r"^(buffer_|global_)")
+# kernels with producer waves: the plain and variable-length K <= 128 kernels of
+# both directions, and the grouped kernel at K = 64 and 128 (mangled names)
+PRODUCER_KERNELS = re.compile(r"correct_h0_(fwd|bwd)_dma|correct_h0_grouped_kernelILi(64|128)E")
 
 
 def _tools():
@@ -59,7 +62,7 @@ def _kernels(text: str):
         if m:
             if cur is not None:
                 yield cur, body
-            cur, body = (m.group(1), []) if re.search(r"correct_h0_(fwd|bwd)_dma", m.group(1)) else (None, [])
+            cur, body = (m.group(1), []) if PRODUCER_KERNELS.search(m.group(1)) else (None, [])
             continue
         if cur is not None:
             ins = raw.split("//")[0].strip()
@@ -101,8 +104,8 @@ def test_producer_barriers_cover_every_copy(name, tmp_path):
     if not os.path.exists(lib):
         pytest.skip(f"{name} is not built")
     kernels = list(_kernels(_disassemble(lib, tmp_path)))
-    # {fwd, bwd} x K in {64, 128} x {kv, vk}, plain and variable-length
-    assert len(kernels) == 16, [k for k, _ in kernels]
+    # {fwd, bwd} x K in {64, 128} x {kv, vk}, plain and variable-length; grouped at K = 64, 128
+    assert len(kernels) == 18, [k for k, _ in kernels]
     for sym, body in kernels:
         checked, problems = _check(body)
         # the barrier after the first copy and the one in the step loop, at least
