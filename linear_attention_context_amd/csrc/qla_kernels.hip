@@ -181,7 +181,8 @@ __device__ __forceinline__ void st4(float* p, f4 v) { *reinterpret_cast<f4*>(p) 
 
 // Optional forced-delay schedule (built only into the race-test library): one
 // wave per step sleeps before reading the shared state slot, another before
-// writing the next one.  Results must not change.
+// writing the next one, and one producer before its copy.  Results must not
+// change.
 __device__ __forceinline__ void debug_delay(int wave, int s, int which)
 {
 #if defined(QLA_DEBUG_DELAY) && QLA_DEBUG_DELAY
@@ -918,6 +919,7 @@ struct DmaChain {
         warm_h(C, sink, HA, p, tile, V);
         asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(QLA_M_TOUCH + 1) : "memory");
         for (int s = 0; s + 1 < C.n_seg; ++s) {
+            debug_delay(p, s, 2);  // a late copy: the MFMA waves must wait for it at the barrier
             dma_unit(C.M + (size_t)sg(C, s + 1) * K * K, stages + ((s + 1) & 1) * STAGE, p);
             copies_before_warmups();
             if constexpr (QLA_M_TOUCH > 0) warm_m(C, sink, s + 1 + QLA_M_TOUCH, p, tile, tiles);
