@@ -11,8 +11,9 @@ of their own, 16 x 52.4 MB = 839 MB > the 256 MB MALL, so every call streams
 its inputs from HBM.  The same calls on one resident set (warm) and the
 bandwidth of a plain 1 GiB device copy are reported beside it.
 
-Timing: --warmup untimed steps first (640 by default: per-call times keep
-falling for the first thousand or so calls of a process, about 20 ms), then the steps'
+Timing: --warmup untimed steps first (640 by default: calls on freshly
+allocated buffers keep getting faster for the first thousand or so calls
+over them, about 20 ms), then the steps'
 kv calls back to back, then their vk calls, with HIP events on the launch
 stream at the boundaries (--mode direct, default).
 --mode graph follows the pages' protocol instead: each variant's launches are
@@ -143,7 +144,6 @@ def run_sweep(args) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    settle = True
     K = V = 128
     copy_gbps = measured_copy_gbps(torch, dev)
     for tokens in qi.SWEEP_TOKENS:
@@ -158,6 +158,12 @@ def run_sweep(args) -> int:
                 sets = [dict(H=torch.from_numpy(Hl).to(dev), M=torch.from_numpy(M).to(dev),
                              S0=torch.from_numpy(Sl).to(dev), out=torch.empty(Hl.shape, device=dev))
                         for _ in range(rot)]
+                # untimed: calls on freshly allocated buffers run slow until about a
+                # thousand calls have gone over them
+                for i in range(1024):
+                    x = sets[i % rot]
+                    qla.qla_correct_h0(x["H"], x["M"], x["S0"], x["out"], layout, "fwd", 1, heads, n, K, V,
+                                       stream=stream.cuda_stream)
                 for direction in ("fwd", "bwd"):
                     for s0_on in (True, False):
                         def call(x):
@@ -165,11 +171,8 @@ def run_sweep(args) -> int:
                                                direction, 1, heads, n, K, V, stream=stream.cuda_stream)
                         times = {}
                         for label, order in (("warm", [0] * 64), ("rotated", [i % rot for i in range(max(64, rot))])):
-                            # untimed; the first point also lets the per-call times of the
-                            # process settle (about a thousand calls)
-                            for i in range(1024 if settle else 64):
+                            for i in range(64):  # untimed
                                 call(sets[order[i % len(order)]])
-                            settle = False
                             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                             e0.record(stream)
                             for i in order:
@@ -237,8 +240,8 @@ def run_configs(args) -> int:
                     qla.qla_correct_h0(x["H"], x["M"], x["S0"], x["out"], what[0], what[1], B, NH, N, K, V,
                                        stream=stream.cuda_stream)
             reps = 64 if nbytes < (64 << 20) else 8
-            # untimed calls first: per-call times settle only after the first
-            # thousand or so short calls of a process (about 20 ms)
+            # untimed calls first: calls on freshly allocated buffers run slow
+            # until about a thousand calls have gone over them
             n_warm = 1024 if nbytes < (64 << 20) else 8
             times = {}
             for kind, order in (("warm", [0] * reps), ("rotated", [i % rot for i in range(max(reps, rot))])):
