@@ -59,6 +59,7 @@ typedef unsigned u2 __attribute__((ext_vector_type(2)));
 #ifndef QLA_LDS_PAD
 #define QLA_LDS_PAD 8
 #endif
+// Cache-policy bits of the general kernel's M and H loads (0: default).
 #ifndef QLA_MLOAD_AUX
 #define QLA_MLOAD_AUX 0
 #endif
@@ -70,6 +71,7 @@ typedef unsigned u2 __attribute__((ext_vector_type(2)));
 #ifndef QLA_STORE_AUX
 #define QLA_STORE_AUX 0
 #endif
+// K <= 128: run the producer kernels (1) or the general kernel (0).
 #ifndef QLA_FWD_DMA
 #define QLA_FWD_DMA 1
 #endif
@@ -79,8 +81,8 @@ typedef unsigned u2 __attribute__((ext_vector_type(2)));
 #ifndef QLA_DMA_WAVES
 #define QLA_DMA_WAVES 4
 #endif
-// Forward K <= 128: H is loaded this many steps ahead, and M_j's lines are
-// warmed into L2 this many steps ahead of its copy (0: off).
+// Producer kernels (K <= 128): H is loaded this many steps ahead, and M_j's
+// lines are warmed into L2 this many steps ahead of its copy (0: off).
 #ifndef QLA_H_AHEAD
 #define QLA_H_AHEAD 3
 #endif
@@ -92,20 +94,22 @@ typedef unsigned u2 __attribute__((ext_vector_type(2)));
 #endif
 constexpr int kTileV = 16;  // kv-view columns per workgroup
 
-// Waves per workgroup.  Forward at K >= 128 runs two waves per SIMD, so one
-// wave's operand waits are covered by the other's MFMAs.  Backward keeps
-// four: its M share is a column block, and 32 columns per wave make each
-// load a whole 128-byte line per row (16 columns would halve that).  The
-// grouped kernel has one block size for all its groups and uses eight.
+// MFMA waves per workgroup.  The producer kernels (K <= 128, both
+// directions) use QLA_WAVES(K, true): 8 at K = 128, two per SIMD, so one
+// wave's operand waits are covered by the other's MFMAs; 4 at K = 64.  The
+// general kernel (K = 256) runs 8 forward and 4 backward: its backward M
+// share is a column block, and 32 columns per wave make each load a whole
+// 128-byte line per row (16 columns would halve that).  The grouped kernel at
+// K = 256 has one block size for all its groups and uses eight.
 #ifndef QLA_WAVES
 #define QLA_WAVES(K, FWD) ((K) >= 128 && (FWD) ? 8 : 4)
 #endif
 #ifndef QLA_GROUPED_WAVES
 #define QLA_GROUPED_WAVES(K) ((K) >= 128 ? 8 : 4)
 #endif
-// Prefetch distance in units (panels) of M.  Backward at K = 128 prefetches
-// one step ahead: with the L2 warm-up two steps ahead of that, a deeper
-// register ring measured slower.
+// Prefetch distance of the general kernel in units (panels) of M: one panel
+// at K = 256.  The K <= 128 values apply only with the producer kernels
+// switched off (backward at K = 128 measured best one step ahead there).
 #ifndef QLA_PREFETCH_UNITS
 #define QLA_PREFETCH_UNITS(K, FWD) ((K) >= 256 ? 1 : (K) >= 128 ? ((FWD) ? 3 : 1) : 3)
 #endif
