@@ -28,15 +28,17 @@
 // no wave reaches before its writes landed.  Read-before-reuse holds by
 // construction.
 //
-// Staging of M.  At K <= 128 (DmaChain, both directions), dedicated producer waves copy
-// each M_j into one of two LDS stages, released by that same per-step barrier
-// (the pages' Hopper kernel also had a producer, with its own two-slot
-// buffers and hand-off; the slot-reuse race the note diagnoses, section
+// Staging of M.  At K <= 128 (DmaChain, both directions, also inside the
+// grouped kernel), dedicated producer waves copy each M_j into one of two LDS
+// stages, released by that same per-step barrier (the pages' Hopper kernel
+// also had a producer, with its own two-slot buffers and hand-off; the
+// slot-reuse race the note diagnoses, section
 // "决定性证据：错误值来自同一槽位的下一代", a slot read after it was refilled with
 // the segment two steps away, cannot happen here because a stage is refilled
 // only after the barrier that every reader of its previous contents has
-// passed).  Elsewhere (Tile) each wave prefetches exactly the share of M it
-// consumes into a private register ring, forward through a private LDS slot.
+// passed), and warm later steps' lines into L2 right behind each copy.  At
+// K = 256 (Tile) each wave prefetches exactly the share of M it consumes into
+// a private register ring, forward through a private LDS slot.
 //
 // Matrix cores: v_mfma_f32_16x16x4_f32 (fp32 in, fp32 accumulate).  Lane l =
 // 16*g + c feeds A(row c, k) and B(k, column c) with k = 4g + q on the q-th of
