@@ -73,7 +73,8 @@ def parse_args(argv=None):
                    help="instead of the step: time every workload configuration (tiny, 32K x 32 heads fwd and bwd, "
                         "long chain, wide grouped), one JSON line per configuration and variant")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="also run a plain 1 GiB device copy (for scaling rocprof byte counters)")
+                   help="also run a plain 1 GiB device copy (for scaling rocprof byte counters); "
+                        "with --configs, after the configurations")
     return p.parse_args(argv)
 
 
@@ -265,7 +266,21 @@ def run_configs(args) -> int:
             }), flush=True)
             del sets
             torch.cuda.empty_cache()
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     return 0
+
+
+def copy_calibration(torch, dev):
+    """A plain 1 GiB device-to-device copy, the reference for scaling rocprof byte counters."""
+    n = 1 << 28  # 1 GiB of fp32
+    a = torch.empty(n, device=dev)
+    b = torch.empty(n, device=dev)
+    a.fill_(1.0)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    return {"read": 4 * n, "written": 4 * n}
 
 
 def main(argv=None):
@@ -548,14 +563,7 @@ def main(argv=None):
         }
 
     if args.copy_calibration:
-        n = 1 << 28  # 1 GiB of fp32
-        a = torch.empty(n, device=dev)
-        b = torch.empty(n, device=dev)
-        a.fill_(1.0)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = {"read": 4 * n, "written": 4 * n}
+        result["copy_calibration_bytes"] = copy_calibration(torch, dev)
 
     print(json.dumps(result), flush=True)
     return 0
