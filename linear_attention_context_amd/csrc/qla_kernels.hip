@@ -498,7 +498,11 @@ struct Tile {
 
     static constexpr int kLinesT = K * K * 4 / 128;  // 128-byte lines of one M
     static constexpr int kTouchT = (kLinesT + 64 * S::WAVES - 1) / (64 * S::WAVES);
-    static constexpr int TD = (D + NP - 1) / NP + 2;  // steps ahead of the touch
+    // Steps ahead of the touch: at K = 256 one step before the prefetch (two
+    // steps' worth of M, H and out for two chains already fill much of an
+    // XCD's 4 MiB L2; warming earlier lets lines fall out before all 16 tiles
+    // have loaded them), elsewhere two.
+    static constexpr int TD = (D + NP - 1) / NP + (K >= 256 ? 1 : 2);
 
     // Working registers, carried from step to step.
     struct StepCtx {
