@@ -64,3 +64,31 @@ def test_grouped_in_place():
     qla.qla_correct_h0_grouped(Hd, Md, Sd, Hd, GROUPS, batch, heads, n, K, K)
     torch.cuda.synchronize()
     assert torch.equal(Hd.view(torch.int32), sep.view(torch.int32))
+
+
+@pytest.mark.parametrize("K", [64, 128])
+def test_grouped_matches_plain_calls_bitwise(K):
+    """At K <= 128 a grouped call runs the same per-chain code as plain calls:
+    every group's output equals, bit for bit, a plain call on that group's heads."""
+    import torch
+
+    import linear_attention_context_amd as qla
+    batch, heads, n, V = 2, 7, 5, K + 20
+    H, M, S0 = qi.random_case(900 + K, (batch, heads), n, K, V)
+    # all heads stored in the kv shape; vk groups read their heads' K*V floats as V x K
+    Hd, Md, Sd = to_device(H), to_device(M), to_device(S0)
+    grouped = torch.full_like(Hd, float("nan"))
+    qla.qla_correct_h0_grouped(Hd, Md, Sd, grouped, GROUPS, batch, heads, n, K, V)
+    torch.cuda.synchronize()
+    for begin, count, layout, direction in GROUPS:
+        sl = slice(begin, begin + count)
+        h = to_device(np.ascontiguousarray(H[:, sl]))
+        m = to_device(np.ascontiguousarray(M[:, sl]))
+        s = to_device(np.ascontiguousarray(S0[:, sl]))
+        plain = torch.full_like(h, float("nan"))
+        if layout == "vk":  # the same floats, viewed V x K
+            h, s, plain = h.view(batch, count, n, V, K), s.view(batch, count, V, K), plain.view(batch, count, n, V, K)
+        qla.qla_correct_h0(h, m, s, plain, layout, direction, batch, count, n, K, V)
+        torch.cuda.synchronize()
+        g = grouped[:, sl].contiguous().view(torch.int32).flatten()
+        assert torch.equal(g, plain.contiguous().view(torch.int32).flatten()), (K, begin, layout, direction)
