@@ -942,11 +942,11 @@ struct DmaChain {
     // ---- MFMA waves -------------------------------------------------------
     // The step's global accesses go out between MFMA blocks late in the
     // step: out of step s-1 before block kStoreAt, H of step s+HA (already
-    // warmed into L2 by the producers) before block kLoadAt.  Right after the barrier the producers fill the CU's
-    // vector memory queue, and an access waiting for a slot there holds up
-    // this wave; late in the step the queue has drained, and issuing them
-    // between blocks rather than all after the last one lets the other
-    // wave's MFMAs cover their issue.
+    // warmed into L2 by the producers) before block kLoadAt.  Right after the
+    // barrier the producers fill the CU's vector memory queue, and an access
+    // waiting for a slot there holds up this wave; late in the step the queue
+    // has drained, and issuing them between blocks rather than all after the
+    // last one lets the other wave's MFMAs cover their issue.
     static constexpr int kStoreAt = 5 * BP / 8, kLoadAt = 7 * BP / 8;
     static_assert(0 < kStoreAt && kStoreAt < kLoadAt && kLoadAt < BP, "store and load points inside the step");
 
