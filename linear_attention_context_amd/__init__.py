@@ -16,7 +16,7 @@ import os
 
 __all__ = [
     "QLA_LAYOUT_KV", "QLA_LAYOUT_VK", "QLA_DIR_FWD", "QLA_DIR_BWD", "QLA_MAX_GROUPS", "QLA_MAX_SEQS",
-    "QlaError", "qla_correct_h0", "qla_correct_h0_grouped", "qla_correct_h0_varlen", "qla_status_str",
+    "QLA_ERR_MEMORY", "QlaError", "qla_correct_h0", "qla_correct_h0_grouped", "qla_correct_h0_varlen", "qla_status_str",
     "raw_correct_h0", "raw_correct_h0_grouped", "raw_correct_h0_varlen", "load_library", "library_path",
 ]
 
@@ -89,6 +89,27 @@ def _ptr(x):
     raise TypeError(f"expected a tensor, an int address or None, got {type(x)!r}")
 
 
+QLA_ERR_MEMORY = -8
+
+
+def _tensor_ok(x, need: int) -> bool:
+    """A tensor argument must be float32, contiguous, on a GPU and hold at least
+    ``need`` elements (the extent the call reads or writes).  Integer
+    addresses and None are passed through unchecked: the library checks those."""
+    if x is None or isinstance(x, int) or not hasattr(x, "data_ptr"):
+        return True
+    import torch
+    return (x.dtype == torch.float32 and x.is_cuda and x.is_contiguous() and x.numel() >= need)
+
+
+def _extents_ok(H, M, S0, out, states: int, chains: int, K: int, V: int) -> bool:
+    """``states`` segment states of H / out (K*V floats each) and M (K*K), ``chains`` of S0."""
+    if states <= 0 or K <= 0 or V <= 0:
+        return True  # empty or malformed: the library decides
+    return (_tensor_ok(H, states * K * V) and _tensor_ok(out, states * K * V)
+            and _tensor_ok(M, states * K * K) and _tensor_ok(S0, chains * K * V))
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -110,8 +131,12 @@ _DIR_NAMES = {"fwd": QLA_DIR_FWD, "bwd": QLA_DIR_BWD}
 
 def raw_correct_h0(H, M, S0, out, layout, direction, batch, heads, n_seg, K, V, stream=None,
                    lib: ctypes.CDLL | None = None) -> int:
-    """Call qla_correct_h0 and return its status code unchanged."""
+    """Call qla_correct_h0 and return its status code unchanged (QLA_ERR_MEMORY
+    without calling it if a tensor argument is not float32, contiguous, on the
+    GPU and large enough)."""
     lib = lib or load_library()
+    if not _extents_ok(H, M, S0, out, batch * heads * n_seg, batch * heads, K, V):
+        return QLA_ERR_MEMORY
     return lib.qla_correct_h0(_ptr(H), _ptr(M), _ptr(S0), _ptr(out),
                               _enum(layout, _LAYOUT_NAMES), _enum(direction, _DIR_NAMES),
                               batch, heads, n_seg, K, V, _stream(stream))
@@ -138,6 +163,8 @@ def raw_correct_h0_grouped(H, M, S0, out, groups, batch, heads, n_seg, K, V, str
                            lib: ctypes.CDLL | None = None, n_groups: int | None = None) -> int:
     """Call qla_correct_h0_grouped; ``groups`` is a list of (head_begin, head_count, layout, direction)."""
     lib = lib or load_library()
+    if not _extents_ok(H, M, S0, out, batch * heads * n_seg, batch * heads, K, V):
+        return QLA_ERR_MEMORY
     arr = _groups(groups)
     n = len(groups) if n_groups is None else n_groups
     return lib.qla_correct_h0_grouped(_ptr(H), _ptr(M), _ptr(S0), _ptr(out), arr, n,
@@ -164,6 +191,8 @@ def raw_correct_h0_varlen(H, M, S0, out, layout, direction, seg_offsets, heads, 
         n = len(offs) - 1 if n_seqs is None else n_seqs
         # the library reads n + 1 offsets: never past the array (missing ones read as 0)
         arr = (ctypes.c_int * max(len(offs), n + 1, 1))(*offs)
+        if 0 <= n < len(offs) and not _extents_ok(H, M, S0, out, heads * offs[n], n * heads, K, V):
+            return QLA_ERR_MEMORY
     return lib.qla_correct_h0_varlen(_ptr(H), _ptr(M), _ptr(S0), _ptr(out),
                                      _enum(layout, _LAYOUT_NAMES), _enum(direction, _DIR_NAMES),
                                      arr, n, heads, K, V, _stream(stream))
