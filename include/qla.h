@@ -65,8 +65,9 @@ extern "C" {
 #define QLA_OK 0
 #define QLA_ERR_NULL (-1)   /* H, M or out is NULL */
 #define QLA_ERR_ENUM (-2)   /* layout or direction not one of the values above */
-#define QLA_ERR_SHAPE (-3)  /* K not 64/128/256, V not a multiple of 4 in [4, 4096],
-                               a negative count, or a size that overflows */
+#define QLA_ERR_SHAPE (-3)  /* K not a multiple of 16 in [16, 256], V not a multiple
+                               of 4 in [4, 4096], a negative count, or a size that
+                               overflows the launch limits */
 #define QLA_ERR_ALIGN (-4)  /* a pointer not 16-byte aligned */
 #define QLA_ERR_ALIAS (-5)  /* out overlaps H (other than out == H), M or S0 */
 #define QLA_ERR_GROUPS (-6) /* head groups do not partition [0, heads) */
@@ -101,7 +102,7 @@ typedef struct {
  *   batch, heads  : chain grid (>= 0; a zero count, or n_seg == 0, is an empty
  *                   call that returns QLA_OK and enqueues nothing).
  *   n_seg         : segments per chain (>= 0).
- *   K             : key dimension (size of M), one of 64, 128, 256.
+ *   K             : key dimension (size of M), a multiple of 16 in [16, 256].
  *   V             : value dimension, a multiple of 4 in [4, 4096].
  *   stream        : hipStream_t to enqueue on.
  * Returns QLA_OK or a QLA_ERR_* code.

@@ -33,12 +33,18 @@ def hipcc_command(out: str, defines=()) -> list:
     return cmd
 
 
-def _compile(out: str, defines=()) -> None:
+def _start(out: str, defines=()):
     tmp = out + f".tmp{os.getpid()}"
-    proc = subprocess.run(hipcc_command(tmp, defines), capture_output=True, text=True)
+    proc = subprocess.Popen(hipcc_command(tmp, defines), stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    return out, tmp, proc
+
+
+def _finish(job) -> None:
+    out, tmp, proc = job
+    _, stderr = proc.communicate()
     # The host pass reports the device-only feature flag as unknown; that line is expected.
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
-    err = "\n".join(l for l in proc.stderr.splitlines() if noise not in l)
+    err = "\n".join(l for l in stderr.splitlines() if noise not in l)
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed for {out}:\n{err}")
     if err.strip():
@@ -47,8 +53,10 @@ def _compile(out: str, defines=()) -> None:
 
 
 def build() -> str:
-    _compile(LIB)
-    _compile(LIB_DELAY, defines=("QLA_DEBUG_DELAY=1",))
+    # the two libraries compile in parallel
+    jobs = [_start(LIB), _start(LIB_DELAY, defines=("QLA_DEBUG_DELAY=1",))]
+    for job in jobs:
+        _finish(job)
     return LIB
 
 

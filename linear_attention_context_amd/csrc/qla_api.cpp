@@ -13,16 +13,19 @@ namespace {
 bool valid_layout(int v) { return v == QLA_LAYOUT_KV || v == QLA_LAYOUT_VK; }
 bool valid_direction(int v) { return v == QLA_DIR_FWD || v == QLA_DIR_BWD; }
 
-// Shape limits: K selects a compiled kernel; V is tiled by 16 columns with a
-// ragged last tile handled in 4-float vectors.
+// Shape limits: K (a multiple of 16 in [16, 256]) selects a compiled kernel
+// family; V is tiled by 16 columns with a ragged last tile handled in 4-float
+// vectors.
 int check_shape(int batch, int heads, int n_seg, int K, int V)
 {
     if (batch < 0 || heads < 0 || n_seg < 0) return QLA_ERR_SHAPE;
-    if (K != 64 && K != 128 && K != 256) return QLA_ERR_SHAPE;
+    if (K < 16 || K > 256 || K % 16 != 0) return QLA_ERR_SHAPE;
     if (V < 4 || V > 4096 || V % 4 != 0) return QLA_ERR_SHAPE;
-    // One workgroup per (chain, column tile): the grid must fit an int.
+    // One workgroup per (chain, column tile): the grid must fit an int, and
+    // its work-items (at most 1024 per workgroup) the runtime's 32-bit count.
     const long long chains = (long long)batch * heads;
-    if (chains * qla::tiles_for(V) > INT32_MAX) return QLA_ERR_SHAPE;
+    const long long groups = chains * qla::tiles_for(V);
+    if (groups > INT32_MAX || groups * qla::max_threads_per_group() > (long long)UINT32_MAX) return QLA_ERR_SHAPE;
     return QLA_OK;
 }
 
@@ -170,8 +173,8 @@ const char* qla_status_str(int status)
     case QLA_OK: return "ok";
     case QLA_ERR_NULL: return "H, M or out is NULL";
     case QLA_ERR_ENUM: return "layout or direction is not a known value";
-    case QLA_ERR_SHAPE: return "unsupported shape (K must be 64, 128 or 256; V a multiple of 4 in [4, 4096]; "
-                               "counts >= 0; grid within int range)";
+    case QLA_ERR_SHAPE: return "unsupported shape (K must be a multiple of 16 in [16, 256]; V a multiple of 4 in "
+                               "[4, 4096]; counts >= 0; grid within the launch limits)";
     case QLA_ERR_ALIGN: return "a buffer is not 16-byte aligned";
     case QLA_ERR_ALIAS: return "out overlaps H (other than exactly in place), M or S0";
     case QLA_ERR_GROUPS: return "head groups do not partition [0, heads) (or too many groups)";

@@ -42,6 +42,8 @@ struct SeqTable {
 };
 
 int tiles_for(int V);
+// Largest workgroup any kernel of the library launches (threads).
+int max_threads_per_group();
 hipError_t launch_correct_h0(const LaunchArgs& a);
 hipError_t launch_correct_h0_grouped(const LaunchArgs& a, const GroupTable& table);
 hipError_t launch_correct_h0_varlen(const LaunchArgs& a, const SeqTable& seqs);

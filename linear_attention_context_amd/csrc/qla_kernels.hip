@@ -58,63 +58,33 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 typedef unsigned u2 __attribute__((ext_vector_type(2)));
 
-#ifndef QLA_LDS_PAD
-#define QLA_LDS_PAD 8
-#endif
-// Cache-policy bits of the general kernel's M and H loads (0: default).
-#ifndef QLA_MLOAD_AUX
-#define QLA_MLOAD_AUX 0
-#endif
-#ifndef QLA_HLOAD_AUX
-#define QLA_HLOAD_AUX 0
-#endif
-// Plain stores for out: with inputs streamed from HBM they beat
-// non-temporal ones (kv tiles write 64-byte halves of lines that L2 merges).
-#ifndef QLA_STORE_AUX
-#define QLA_STORE_AUX 0
-#endif
-// K <= 128: run the producer kernels (1) or the general kernel (0).
-#ifndef QLA_FWD_DMA
-#define QLA_FWD_DMA 1
-#endif
-#ifndef QLA_BWD_DMA
-#define QLA_BWD_DMA 1
-#endif
-#ifndef QLA_DMA_WAVES
-#define QLA_DMA_WAVES 4
-#endif
-// Producer kernels (K <= 128): H is loaded this many steps ahead, and M_j's
-// lines are warmed into L2 this many steps ahead of its copy (0: off).
-#ifndef QLA_H_AHEAD
-#define QLA_H_AHEAD 3
-#endif
-#ifndef QLA_M_TOUCH
-#define QLA_M_TOUCH 2
-#endif
-#ifndef QLA_MO_AHEAD
-#define QLA_MO_AHEAD 2
-#endif
-constexpr int kTileV = 16;  // kv-view columns per workgroup
+constexpr int kTileV = 16;     // kv-view columns per workgroup
+constexpr int kLdsPad = 8;     // LDS state row stride K + 8 floats: conflict-free 16-byte operand reads
+constexpr int kProducers = 4;  // producer waves of the K <= 128 kernels
+// K <= 128 kernels: H is loaded kHAhead steps ahead, and M_j's lines are
+// warmed into L2 kMTouch steps ahead of its copy.
+constexpr int kHAhead = 3;
+constexpr int kMTouch = 2;
+constexpr int kMoAhead = 2;    // general kernel: staged M operand reads run this many blocks ahead
 
-// MFMA waves per workgroup.  The producer kernels (K <= 128, both
-// directions) use QLA_WAVES(K, true): 8 at K = 128, two per SIMD, so one
-// wave's operand waits are covered by the other's MFMAs; 4 at K = 64.  The
-// general kernel (K = 256) runs 8 forward and 4 backward: its backward M
-// share is a column block, and 32 columns per wave make each load a whole
-// 128-byte line per row (16 columns would halve that).  The grouped kernel at
-// K = 256 has one block size for all its groups and uses eight.
-#ifndef QLA_WAVES
-#define QLA_WAVES(K, FWD) ((K) >= 128 && (FWD) ? 8 : 4)
-#endif
-#ifndef QLA_GROUPED_WAVES
-#define QLA_GROUPED_WAVES(K) ((K) >= 128 ? 8 : 4)
-#endif
-// Prefetch distance of the general kernel in units (panels) of M: one panel
-// at K = 256.  The K <= 128 values apply only with the producer kernels
-// switched off (backward at K = 128 measured best one step ahead there).
-#ifndef QLA_PREFETCH_UNITS
-#define QLA_PREFETCH_UNITS(K, FWD) ((K) >= 256 ? 1 : (K) >= 128 ? ((FWD) ? 3 : 1) : 3)
-#endif
+// Compute sizes.  K <= 128 (every multiple of 16) runs the producer kernels
+// with K/16 MFMA waves of 16 rows each.  K = 256 runs the general kernel,
+// 8 MFMA waves forward and 4 backward: its backward M share is a column
+// block, and 32 columns per wave make each load a whole 128-byte line per row
+// (16 columns would halve that).  128 < K < 256 runs the same general kernel
+// at compute size 256 with the missing rows and columns read as zeros (a
+// zero-padded M and state give exactly the unpadded result in the first K
+// rows).  The grouped kernel at K > 128 has one block size for all its
+// groups and uses eight waves.
+constexpr int general_waves(bool fwd) { return fwd ? 8 : 4; }
+constexpr int kGroupedWaves = 8;
+// Prefetch distance of the general kernel, in units (64-k panels) of M.
+constexpr int kPrefetchUnits = 1;
+constexpr int pow2_divisor(int x) { return x % 2 ? 1 : 2 * pow2_divisor(x / 2); }
+// XOR swizzle of a row's 16-byte chunks in an M stage: by the row's low bits,
+// as many as keep the chunk index inside the row (a power of two dividing the
+// row's K/4 chunks), at most the low four.
+constexpr int stage_swizzle(int kp) { return pow2_divisor(kp / 4) < 16 ? pow2_divisor(kp / 4) : 16; }
 
 template <int K, int WAVES_, bool FWD_>
 struct Shape {
@@ -125,17 +95,18 @@ struct Shape {
     static constexpr int KP = K >= 256 ? 64 : K;  // k-width of one M panel
     static constexpr int NP = K / KP;             // panels per step
     static constexpr int BP = KP / 16;            // 16-wide k blocks per panel
-    static constexpr int LS = K + QLA_LDS_PAD;    // LDS row stride (floats)
+    static constexpr int LS = K + kLdsPad;        // LDS row stride (floats)
+    static constexpr int SWZ = stage_swizzle(KP); // chunk swizzle of a staged M row
     static constexpr int STATE_FLOATS = 2 * kTileV * LS;  // two state slots
     static constexpr int STAGE_FLOATS = ROWS * KP;          // one wave's M panel share
     // Forward staging slots per wave: two (the next panel is written while
     // this one is read) when they fit in the 160 KiB of LDS, else one.
     static constexpr int SS =
-        (STATE_FLOATS + WAVES * 2 * STAGE_FLOATS) * 4 <= 160 * 1024 && QLA_PREFETCH_UNITS(K, FWD_) >= 2 ? 2 : 1;
-    static constexpr int RPI = 256 / KP;                    // M rows per coalesced load instruction
+        (STATE_FLOATS + WAVES * 2 * STAGE_FLOATS) * 4 <= 160 * 1024 && kPrefetchUnits >= 2 ? 2 : 1;
+    static constexpr int RPI = KP >= 64 ? 256 / KP : 1;    // M rows per coalesced load instruction (general kernel)
     // Prefetch distance in panels (see Tile::prefetch).
-    static constexpr int D = QLA_PREFETCH_UNITS(K, FWD_);
-    static_assert(ROWS % 16 == 0, "K must be a multiple of 64");
+    static constexpr int D = kPrefetchUnits;
+    static_assert(K % 16 == 0 && ROWS % 16 == 0, "whole 16-row tiles per wave");
     static_assert(NP <= 4, "at most four panels per step");
 };
 
@@ -175,13 +146,16 @@ __device__ __forceinline__ float bload1(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, AUX));
 }
+// out is written with plain (cached) stores: with inputs streamed from HBM they
+// beat non-temporal and write-through ones (a kv tile writes 64-byte halves of
+// lines that L2 merges with the neighbouring tile's halves).
 __device__ __forceinline__ void bstore1(__amdgpu_buffer_rsrc_t r, unsigned off, float v)
 {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, QLA_STORE_AUX);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, 0);
 }
 __device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, unsigned off, f4 v)
 {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, (int)off, 0, QLA_STORE_AUX);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, (int)off, 0, 0);
 }
 __device__ __forceinline__ void st4(float* p, f4 v) { *reinterpret_cast<f4*>(p) = v; }
 
@@ -203,14 +177,16 @@ __device__ __forceinline__ void debug_delay(int wave, int s, int which)
 #endif
 }
 
-template <int K, int LAYOUT, int DIR, int WAVES>
+// PAD: the caller's head dimension kp (a multiple of 16, below K) is smaller
+// than the compute size K; rows and columns kp .. K-1 of M and of the state
+// are read as zeros and never written.
+template <int K, int LAYOUT, int DIR, int WAVES, bool PAD = false>
 struct Tile {
     using S = Shape<K, WAVES, DIR == QLA_DIR_FWD>;
     static constexpr int T = S::T, KP = S::KP, NP = S::NP, BP = S::BP, LS = S::LS;
     static constexpr bool KV = LAYOUT == QLA_LAYOUT_KV;
     static constexpr bool FWD = DIR == QLA_DIR_FWD;
     static constexpr bool STAGE = FWD;  // forward M goes through LDS staging
-    static constexpr unsigned kMatBytes = (unsigned)K * K * 4u;
     // LDS: two state slots, plus one M staging slot per wave when forward.
     static constexpr int SS = S::SS;
     static constexpr int SF = S::STAGE_FLOATS;
@@ -226,7 +202,15 @@ struct Tile {
         unsigned mcoal;    // byte offset of the lane's first coalesced M chunk (forward)
         int prot, brot;    // k-order rotation of this wave: panels, then 16-k blocks in a panel
         unsigned state_bytes;
+        int kp;            // the caller's K (physical row length of M and of the state)
+        int mrow, mcol;    // PAD, forward: M row and column of the lane's first coalesced chunk
     };
+
+    // Physical K, and the byte size of one M.
+    static __device__ __forceinline__ int kph(const Lane& L) { return PAD ? L.kp : K; }
+    static __device__ __forceinline__ unsigned mat_bytes(const Lane& L) { return (unsigned)kph(L) * kph(L) * 4u; }
+    static __device__ __forceinline__ unsigned wrapb(int x) { return (unsigned)x % (unsigned)BP; }
+    static __device__ __forceinline__ unsigned wrapp(int x) { return (unsigned)x % (unsigned)NP; }
 
     // Row of the kv view held by fragment row i of tile t: tiles are
     // contiguous 16-row blocks forward; backward they interleave with stride
@@ -248,7 +232,7 @@ struct Tile {
     static constexpr int vec_of(int t, int r) { return (KV || FWD) ? t : (T * r + t) >> 2; }
     static constexpr int comp_of(int t, int r) { return (KV || FWD) ? r : (T * r + t) & 3; }
 
-    static __device__ __forceinline__ Lane make_lane(int v0, int V)
+    static __device__ __forceinline__ Lane make_lane(int v0, int V, int kp = K)
     {
         Lane L;
         const int lane = threadIdx.x & 63;
@@ -256,26 +240,32 @@ struct Tile {
         L.g = lane >> 4;
         L.c = lane & 15;
         L.a0 = L.wave * S::ROWS;
-        L.state_bytes = (unsigned)K * V * 4u;
+        L.kp = kp;
+        const int kk = kph(L);
+        L.state_bytes = (unsigned)kk * V * 4u;
         const bool valid = v0 + L.c < V;
 #pragma unroll
         for (int i = 0; i < T; ++i) {
-            const int e = FWD ? (v0 + L.c) * K + L.a0 + 16 * i + 4 * L.g : (v0 + L.c) * K + L.a0 + 4 * T * L.g + 4 * i;
-            L.hoff[i] = valid ? 4u * (unsigned)e : kOutOfRange;
+            const int a = FWD ? L.a0 + 16 * i + 4 * L.g : L.a0 + 4 * T * L.g + 4 * i;  // first of 4 rows
+            L.hoff[i] = valid && (!PAD || a < kk) ? 4u * (unsigned)((v0 + L.c) * kk + a) : kOutOfRange;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                L.hk[i][r] = valid ? 4u * (unsigned)(arow(L.a0, i, 4 * L.g + r) * V + v0 + L.c) : kOutOfRange;
+            for (int r = 0; r < 4; ++r) {
+                const int ar = arow(L.a0, i, 4 * L.g + r);
+                L.hk[i][r] = valid && (!PAD || ar < kk) ? 4u * (unsigned)(ar * V + v0 + L.c) : kOutOfRange;
+            }
         }
         // Forward: M[a0 + c][4g]; backward: M[4g][a0 + T*c] (panel/block/tile offsets added per load).
-        L.moff = 4u * (unsigned)(4 * L.g * K + L.a0 + T * L.c);
+        L.moff = 4u * (unsigned)(4 * L.g * kk + L.a0 + T * L.c);
         // Backward own-row block t, instruction q: k = a0 + T*(4g + q) + t.
-        L.mown = 4u * (unsigned)((L.a0 + 4 * T * L.g) * K + L.a0 + T * L.c);
+        L.mown = 4u * (unsigned)((L.a0 + 4 * T * L.g) * kk + L.a0 + T * L.c);
         // Each wave walks the k range starting at its own rows (k = a0 ...):
         // the state of those rows is its own output, readable before the
         // other waves have written theirs.
         L.prot = (L.wave * S::ROWS / KP) % NP;
         L.brot = (L.wave * S::ROWS / 16) % BP;
-        L.mcoal = 4u * (unsigned)((L.a0 + lane / (KP / 4)) * K + 4 * (lane % (KP / 4)));
+        L.mrow = L.a0 + lane / (KP / 4);
+        L.mcol = 4 * (lane % (KP / 4));
+        L.mcoal = 4u * (unsigned)(L.mrow * kk + L.mcol);
         return L;
     }
 
@@ -285,8 +275,8 @@ struct Tile {
     template <int I>
     static __device__ __forceinline__ void load_state_one(f4 (&h)[T], __amdgpu_buffer_rsrc_t r, const Lane& L)
     {
-        if constexpr (KV) h[I / 4][I % 4] = bload1<QLA_HLOAD_AUX>(r, L.hk[I / 4][I % 4]);
-        else h[I] = bload4<QLA_HLOAD_AUX>(r, L.hoff[I]);
+        if constexpr (KV) h[I / 4][I % 4] = bload1(r, L.hk[I / 4][I % 4]);
+        else h[I] = bload4(r, L.hoff[I]);
     }
 
     static __device__ __forceinline__ void load_state(f4 (&h)[T], __amdgpu_buffer_rsrc_t r, const Lane& L)
@@ -323,20 +313,17 @@ struct Tile {
     // (16 rows, same chunk) spread over all banks.  The slot is private to
     // the wave and LDS executes one wave's accesses in order, so the next
     // panel's writes cannot overtake this panel's reads: no barrier needed.
-    static __device__ __forceinline__ int stage_off(int row, int chunk) { return row * KP + 4 * (chunk ^ (row & 15)); }
+    static __device__ __forceinline__ int stage_off(int row, int chunk) { return row * KP + 4 * (chunk ^ (row & (S::SWZ - 1))); }
 
     // MFMA operand (a, k) = M[a0 + 16t + c][p*KP + 16b + 4g + q] for one (t, b).
     static __device__ __forceinline__ f4 stage_read(const float* stage, int t, int b, const Lane& L)
     {
-        return *reinterpret_cast<const f4*>(stage + stage_off(16 * t + L.c, 4 * ((b + L.brot) & (BP - 1)) + L.g));
+        return *reinterpret_cast<const f4*>(stage + stage_off(16 * t + L.c, 4 * wrapb(b + L.brot) + L.g));
     }
 
     // Position of k block (panel p, block b of the wave's walk) in the k range.
-    static __device__ __forceinline__ int panel_of(int p, const Lane& L) { return (p + L.prot) & (NP - 1); }
-    static __device__ __forceinline__ int kblock(int p, int b, const Lane& L)
-    {
-        return panel_of(p, L) * BP + ((b + L.brot) & (BP - 1));
-    }
+    static __device__ __forceinline__ int panel_of(int p, const Lane& L) { return wrapp(p + L.prot); }
+    static __device__ __forceinline__ int kblock(int p, int b, const Lane& L) { return panel_of(p, L) * BP + wrapb(b + L.brot); }
 
     // Write the lane's fragment of the state into one LDS slot ([v][k] order):
     // element (t, r) is column v = c, row a = arow(t, 4g + r).
@@ -413,7 +400,7 @@ struct Tile {
     // Forward, one panel per step, two staging slots: the first two staged
     // M operand blocks of a step are read at the end of the previous step.
     static constexpr bool kMoCarried = STAGE && SS == 2 && NP == 1;
-    static constexpr int MA = QLA_MO_AHEAD < BP ? QLA_MO_AHEAD : BP;  // staged reads run MA blocks ahead
+    static constexpr int MA = kMoAhead < BP ? kMoAhead : BP;  // staged reads run MA blocks ahead
 
     // ---- one load / staging-write instruction at a time -------------------
     // Loads of one M panel (this wave's share): forward, T*BP whole-line
@@ -425,23 +412,31 @@ struct Tile {
     static __device__ __forceinline__ void load_m(f4 (&m)[T][BP], __amdgpu_buffer_rsrc_t Mr, const Lane& L)
     {
         const int pa = panel_of(TP, L);
+        const int kk = kph(L);
         if constexpr (STAGE) {
-            m[I / BP][I % BP] = bload4<QLA_MLOAD_AUX>(Mr, L.mcoal + 4u * (unsigned)(I * S::RPI * K + pa * KP));
+            unsigned off = L.mcoal + 4u * (unsigned)(I * S::RPI * kk + pa * KP);
+            if constexpr (PAD)
+                if (L.mrow + I * S::RPI >= kk || pa * KP + L.mcol >= kk) off = kOutOfRange;
+            m[I / BP][I % BP] = bload4(Mr, off);
         } else {
             // operand (a, k) = M[k][a], a = a0 + T*c + t; k = 16*kblock + 4g + q,
             // or the own-row order for the first kOwn blocks of panel 0
             constexpr int b = I / 4, q = I % 4;
-            const unsigned off = (TP == 0 && b < kOwn)
-                                     ? L.mown + 4u * (unsigned)((T * q + b) * K)
-                                     : L.moff + 4u * (unsigned)((pa * KP + 16 * ((b + L.brot) & (BP - 1)) + q) * K);
+            const bool own = TP == 0 && b < kOwn;
+            unsigned off = own ? L.mown + 4u * (unsigned)((T * q + b) * kk)
+                               : L.moff + 4u * (unsigned)((pa * KP + 16 * (int)wrapb(b + L.brot) + q) * kk);
+            if constexpr (PAD) {
+                const int k = own ? L.a0 + T * (4 * L.g + q) + b : pa * KP + 16 * (int)wrapb(b + L.brot) + 4 * L.g + q;
+                if (k >= kk || L.a0 + T * L.c >= kk) off = kOutOfRange;
+            }
             if constexpr (T == 1) {
-                m[0][b][q] = bload1<QLA_MLOAD_AUX>(Mr, off);
+                m[0][b][q] = bload1(Mr, off);
             } else if constexpr (T == 2) {
-                const f2 x = bload2<QLA_MLOAD_AUX>(Mr, off);
+                const f2 x = bload2(Mr, off);
                 m[0][b][q] = x[0];
                 m[1][b][q] = x[1];
             } else {
-                const f4 x = bload4<QLA_MLOAD_AUX>(Mr, off);
+                const f4 x = bload4(Mr, off);
 #pragma unroll
                 for (int t = 0; t < T; ++t) m[t][b][q] = x[t];
             }
@@ -528,12 +523,14 @@ struct Tile {
     static __device__ __forceinline__ void touch_ahead(float (&y)[kTouchT], const Chain& C, int s, const StepCtx& X,
                                                        const Lane& L)
     {
-        const bool live = QLA_M_TOUCH > 0 && s < C.n_seg;
-        const __amdgpu_buffer_rsrc_t r = rsrc(C.M + (size_t)seg(C, live ? s : 0) * K * K, live ? kMatBytes : 0u);
+        const bool live = s < C.n_seg;
+        const int kk = kph(L);
+        const int lines = PAD ? kk * kk * 4 / 128 : kLinesT;
+        const __amdgpu_buffer_rsrc_t r = rsrc(C.M + (size_t)seg(C, live ? s : 0) * kk * kk, live ? mat_bytes(L) : 0u);
 #pragma unroll
         for (int k = 0; k < kTouchT; ++k) {
             const int line = X.tile + X.tiles * (L.wave + S::WAVES * ((int)(threadIdx.x & 63) + 64 * k));
-            y[k] = bload1(r, line < kLinesT ? 128u * (unsigned)line : kOutOfRange);
+            y[k] = bload1(r, line < lines ? 128u * (unsigned)line : kOutOfRange);
         }
     }
 
@@ -572,7 +569,9 @@ struct Tile {
         auto mfma = [&](int q) {
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                const float pk = (P == 0 && B < kOwn) ? X.own[B][q] : X.pv[P * BP + B][q];
+                float pk;
+                if constexpr (P == 0 && B < kOwn) pk = X.own[B][q];
+                else pk = X.pv[P * BP + B][q];
                 const float mk = STAGE ? X.mo[B % (MA + 1)][t][q] : m[slot][t][B][q];
                 X.acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(mk, pk, X.acc[t], 0, 0, 0);
             }
@@ -608,7 +607,7 @@ struct Tile {
         const int ts = s + (P + D) / NP;
         const bool live = ts < C.n_seg;
         const int tj = live ? seg(C, ts) : 0;
-        const Prefetch pf{rsrc(C.M + (size_t)tj * K * K, live ? kMatBytes : 0u),
+        const Prefetch pf{rsrc(C.M + (size_t)tj * kph(L) * kph(L), live ? mat_bytes(L) : 0u),
                           rsrc(C.H + (size_t)tj * (L.state_bytes / 4), live ? L.state_bytes : 0u)};
         // Forward: this panel's M is read from staging slot (unit & 1),
         // written during the previous panel (two slots) or just below (one).
@@ -674,11 +673,9 @@ struct Tile {
         put_state(nxt, X.acc, L);
 #pragma unroll
         for (int t = 0; t < T; ++t) X.own[t] = X.acc[t];
-        if constexpr (QLA_M_TOUCH > 0) {
 #pragma unroll
-            for (int k = 0; k < kTouchT; ++k) asm volatile("" ::"v"(X.touched[LSX][k]));
-            touch_ahead(X.touched[LSX], C, s + TD, X, L);
-        }
+        for (int k = 0; k < kTouchT; ++k) asm volatile("" ::"v"(X.touched[LSX][k]));
+        touch_ahead(X.touched[LSX], C, s + TD, X, L);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -704,7 +701,7 @@ struct Tile {
             constexpr int TLS = LO / NP, TP = LO % NP;
             const bool live = TLS < C.n_seg;
             const int tj = live ? seg(C, TLS) : 0;
-            const Prefetch pf{rsrc(C.M + (size_t)tj * K * K, live ? kMatBytes : 0u),
+            const Prefetch pf{rsrc(C.M + (size_t)tj * kph(L) * kph(L), live ? mat_bytes(L) : 0u),
                               rsrc(C.H + (size_t)tj * (L.state_bytes / 4), live ? L.state_bytes : 0u)};
             issue_loads<0, kPanelLoads + (TP == 0 ? kStateLoads : 0), TLS, TP>(pf, m, h, L);
             prologue<LO + 1, HI>(C, m, h, L);
@@ -713,12 +710,13 @@ struct Tile {
 
     // Chain `chain` of a call whose chains all have n_seg segments.
     static __device__ __forceinline__ void run(const float* H, const float* M, const float* S0, float* out,
-                                               int n_seg, int V, size_t chain, int tile, float* lds)
+                                               int n_seg, int V, size_t chain, int tile, float* lds, int kp = K)
     {
-        const size_t state = (size_t)K * V;
-        const Chain C{M + chain * (size_t)n_seg * K * K, H + chain * state * n_seg, out + chain * state * n_seg,
+        const size_t kk = PAD ? kp : K;
+        const size_t state = kk * V;
+        const Chain C{M + chain * (size_t)n_seg * kk * kk, H + chain * state * n_seg, out + chain * state * n_seg,
                       n_seg};
-        run_chain(C, S0 ? S0 + chain * state : nullptr, V, tile, lds);
+        run_chain(C, S0 ? S0 + chain * state : nullptr, V, tile, lds, kp);
     }
 
     // One chain given by its base pointers and segment count; S0c is its
@@ -726,9 +724,10 @@ struct Tile {
     // global access below is then out of its buffer resource's range and
     // does nothing (kept branch-free: an early return here costs the compiler
     // its knowledge that the descriptors are uniform).
-    static __device__ __forceinline__ void run_chain(const Chain& C, const float* S0c, int V, int tile, float* lds)
+    static __device__ __forceinline__ void run_chain(const Chain& C, const float* S0c, int V, int tile, float* lds,
+                                                     int kp = K)
     {
-        const Lane L = make_lane(tile * kTileV, V);
+        const Lane L = make_lane(tile * kTileV, V, kp);
 
         f4 m[R][T][BP];
         f4 h[RH][T];
@@ -771,7 +770,8 @@ struct Tile {
     }
 };
 
-// K <= 128, both directions: producer waves and MFMA waves.  Waves CW .. CW+PW-1 of
+// K <= 128 (any multiple of 16), both directions: producer waves and K/16
+// MFMA waves of 16 rows each.  Waves CW .. CW+PW-1 of
 // the workgroup only move M: together they copy each M_j whole from global
 // memory into one of two LDS stages with 16-byte LDS-DMA buffer loads (the
 // data never passes through registers; each producer issues an equal share
@@ -787,14 +787,16 @@ struct Tile {
 // (every MFMA wave finished reading it before arriving), and unit s+1 has
 // landed before the producer arrives at the barrier that opens step s+1.
 // The stage holds M row-major with each row's 16-byte chunks XOR-swizzled
-// by the row's low four bits, so the whole-row copy and the MFMA-layout
-// reads of either direction are free of bank conflicts (backward, the four
-// rows a read instruction touches differ in bits 2-3 of k, which moves their
-// chunks to distinct banks).
+// by the row's low bits (four of them when the row has at least 16 chunks,
+// K >= 64), so at K = 64 and 128 the whole-row copy and the MFMA-layout reads
+// of either direction are free of bank conflicts (backward, the four rows a
+// read instruction touches differ in bits 2-3 of k, which moves their chunks
+// to distinct banks).
 template <int K, int LAYOUT, int DIR = QLA_DIR_FWD>
 struct DmaChain {
-    static constexpr int CW = QLA_WAVES(K, true);
-    static constexpr int PW = QLA_DMA_WAVES;           // producer waves
+    static_assert(K % 16 == 0 && K >= 16 && K <= 128, "producer kernels cover K = 16 .. 128");
+    static constexpr int CW = K / 16;                  // MFMA waves, 16 rows each
+    static constexpr int PW = kProducers;              // producer waves
     using Tl = Tile<K, LAYOUT, QLA_DIR_FWD, CW>;
     using S = typename Tl::S;
     using Lane = typename Tl::Lane;
@@ -812,7 +814,7 @@ struct DmaChain {
             // k & 15 = 4g + q does not depend on the block, so the lane's four
             // byte offsets (tofs) are fixed; the block adds a uniform 16 K-float step.
             static_assert(T == 1, "one row tile per wave");
-            const int kofs = __builtin_amdgcn_readfirstlane(((b + L.brot) & (BP - 1)) * 16 * K * 4);
+            const int kofs = __builtin_amdgcn_readfirstlane((int)Tl::wrapb(b + L.brot) * 16 * K * 4);
             const char* sb = reinterpret_cast<const char*>(st) + kofs;
             f4 v;
 #pragma unroll
@@ -825,12 +827,16 @@ struct DmaChain {
     static constexpr int kOwn = T;
     static constexpr int MA = 2;                      // staged reads run two blocks ahead
     static constexpr int STAGE = K * K;               // floats per M stage
-    static constexpr int WARM = S::STATE_FLOATS + 2 * STAGE;  // 64 floats the warm-up loads land in
-    static constexpr int LDS_FLOATS = WARM + 64;
-    static constexpr int kDma = K * K / 256;          // 1 KiB copies per M
-    static constexpr int HA = QLA_H_AHEAD;            // H is loaded HA steps ahead
+    static constexpr int WARM = S::STATE_FLOATS + 2 * STAGE;  // the sink the warm-up loads land in
+    static constexpr int kDmaAll = K * K / 256;              // 1 KiB copies per M
+    // The sink: 64 floats for the 4-byte warm-ups, 256 when the producers'
+    // copy counts differ and the spare copies (1 KiB, of nothing) land there.
+    static constexpr int LDS_FLOATS = WARM + (kDmaAll % kProducers ? 256 : 64);
+    static constexpr int SWZ = S::SWZ;                // chunk swizzle of a stage row
+    static constexpr int kDma = kDmaAll;
+    static constexpr int kPer = (kDma + PW - 1) / PW; // copies per producer (the last ones may be empty)
+    static constexpr int HA = kHAhead;                // H is loaded HA steps ahead
     static constexpr int HR = HA + 1;                 // H register slots
-    static_assert(kDma % PW == 0, "equal producer shares");
     static constexpr unsigned kMatBytes = (unsigned)K * K * 4u;
 
     struct Ctx {
@@ -866,8 +872,12 @@ struct DmaChain {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)sink, 4, line < kLines ? 128 * line : (int)kOutOfRange,
                                                  0, 0, 0);
     }
-    // kv: one word in each row's 64-byte piece of the tile (rows p + PW*lane);
-    // vk: one word in each 128-byte line of the tile's rows.
+    // kv: one word in each row's 64-byte piece of the tile (rows p + PW*lane).
+    // The piece shares its 128-byte line with the neighbouring tile's, which
+    // sits on the same XCD, so of a pair of tiles each warms every other row
+    // (a tile without a neighbour warms all).  vk: the tile's rows are one
+    // contiguous block of 16 K floats (64 K bytes, a multiple of 128): one
+    // word in each of its K/2 lines.
     static __device__ __forceinline__ void warm_h(const Chain& C, float* sink, int s, int p, int tile, int V)
     {
         const bool live = s < C.n_seg;
@@ -876,11 +886,11 @@ struct DmaChain {
         const int idx = p + PW * (int)(threadIdx.x & 63);
         unsigned off = kOutOfRange;
         if constexpr (LAYOUT == QLA_LAYOUT_KV) {
-            if (idx < K) off = 4u * (unsigned)(idx * V) + 64u * (unsigned)tile;
+            const int tiles = (V + kTileV - 1) / kTileV;
+            const bool mine = (tile ^ 1) >= tiles || ((idx ^ tile) & 1) == 0;
+            if (idx < K && mine) off = 4u * (unsigned)(idx * V) + 64u * (unsigned)tile;
         } else {
-            constexpr int kRowLines = K * 4 / 128;
-            const int i = idx / kRowLines, c = idx % kRowLines, row = kTileV * tile + i;
-            if (i < kTileV && row < V) off = 4u * (unsigned)(row * K) + 128u * (unsigned)c;
+            if (idx < K / 2) off = 64u * (unsigned)K * (unsigned)tile + 128u * (unsigned)idx;
         }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)sink, 4, (int)off, 0, 0, 0);
     }
@@ -888,23 +898,27 @@ struct DmaChain {
     // ---- producer ---------------------------------------------------------
     // Copy M_j into a stage: copy i fills stage floats [256 i, 256 i + 256);
     // lane l's 16 bytes land at float 256 i + 4 l = (row, swizzled chunk).
-    // Producer p issues copies p, p + PW, p + 2 PW, ...
-    static __device__ __forceinline__ void dma_unit(const float* Mj, float* stage, int p)
+    // Producer p issues copies p, p + PW, p + 2 PW, ... (K*K/256 of them in
+    // all).  When PW does not divide that, a producer past the end issues a
+    // copy of nothing (an out-of-range source) into the sink, so every
+    // producer runs the same straight-line instruction sequence.
+    static __device__ __forceinline__ void dma_unit(const float* Mj, float* stage, float* sink, int p)
     {
         const __amdgpu_buffer_rsrc_t r = rsrc(Mj, kMatBytes);
         const int lane = threadIdx.x & 63;
 #pragma unroll
-        for (int k = 0; k < kDma / PW; ++k) {
+        for (int k = 0; k < kPer; ++k) {
             const int i = k * PW + p;
+            const bool real = kDma % PW == 0 || i < kDma;
             const int q = 256 * i + 4 * lane;
             const int row = q / K, chunk = (q % K) / 4;
-            const int src = row * K + 4 * (chunk ^ (row & 15));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (__attribute__((address_space(3))) void*)(stage + 256 * i), 16, 4 * src, 0, 0, 0);
+            const int src = row * K + 4 * (chunk ^ (row & (SWZ - 1)));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(real ? stage + 256 * i : sink),
+                                                     16, real ? 4 * src : (int)kOutOfRange, 0, 0, 0);
         }
     }
 
-    // Each step: the copy, then the warm-ups for M_{s+1+QLA_M_TOUCH} and for
+    // Each step: the copy, then the warm-ups for M_{s+1+kMTouch} and for
     // the H the MFMA waves load next step; the barrier waits for the copy
     // only (vmcnt counts in issue order, so leaving the warm-ups outstanding
     // still covers every copy instruction).
@@ -916,23 +930,23 @@ struct DmaChain {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
     }
-    static constexpr int kWarmPerStep = (QLA_M_TOUCH > 0) + 1;
+    static constexpr int kWarmPerStep = 2;  // warm-up instructions per producer and step
     static __device__ __forceinline__ void producer(const Chain& C, float* lds, int p, int tile, int V)
     {
         float* stages = lds + S::STATE_FLOATS;
         float* sink = lds + WARM;
         const int tiles = (V + kTileV - 1) / kTileV;
-        dma_unit(C.M + (size_t)sg(C, 0) * K * K, stages, p);
+        dma_unit(C.M + (size_t)sg(C, 0) * K * K, stages, sink, p);
         copies_before_warmups();
 #pragma unroll
-        for (int u = 1; u <= QLA_M_TOUCH; ++u) warm_m(C, sink, u, p, tile, tiles);
+        for (int u = 1; u <= kMTouch; ++u) warm_m(C, sink, u, p, tile, tiles);
         warm_h(C, sink, HA, p, tile, V);
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(QLA_M_TOUCH + 1) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kMTouch + 1) : "memory");
         for (int s = 0; s + 1 < C.n_seg; ++s) {
             debug_delay(p, s, 2);  // a late copy: the MFMA waves must wait for it at the barrier
-            dma_unit(C.M + (size_t)sg(C, s + 1) * K * K, stages + ((s + 1) & 1) * STAGE, p);
+            dma_unit(C.M + (size_t)sg(C, s + 1) * K * K, stages + ((s + 1) & 1) * STAGE, sink, p);
             copies_before_warmups();
-            if constexpr (QLA_M_TOUCH > 0) warm_m(C, sink, s + 1 + QLA_M_TOUCH, p, tile, tiles);
+            warm_m(C, sink, s + 1 + kMTouch, p, tile, tiles);
             warm_h(C, sink, s + 1 + HA, p, tile, V);
             asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWarmPerStep) : "memory");
         }
@@ -946,19 +960,25 @@ struct DmaChain {
     // barrier the producers fill the CU's vector memory queue, and an access
     // waiting for a slot there holds up this wave; late in the step the queue
     // has drained, and issuing them between blocks rather than all after the
-    // last one lets the other wave's MFMAs cover their issue.
-    static constexpr int kStoreAt = 5 * BP / 8, kLoadAt = 7 * BP / 8;
-    static_assert(0 < kStoreAt && kStoreAt < kLoadAt && kLoadAt < BP, "store and load points inside the step");
+    // last one lets the other wave's MFMAs cover their issue.  With fewer
+    // than eight blocks (K < 128) the points fall on the nearest block
+    // boundaries, with one block both before it.
+    static constexpr int kStoreAt = 5 * BP / 8;
+    static constexpr int kLoadAt = 7 * BP / 8 > kStoreAt ? 7 * BP / 8 : kStoreAt;
+    static constexpr int kFirstReads = MA < BP ? MA : BP;  // staged operand blocks read right after the barrier
 
-    // MFMA blocks B .. E-1.
+    // MFMA blocks B .. E-1 (none if B >= E).
     template <int B, int E = BP>
     static __device__ __forceinline__ void blocks(Ctx& X, const Lane& L)
     {
+      if constexpr (B < E) {
         constexpr int nr = B + MA < BP ? T : 0;
         auto mfma = [&](int q) {
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                const float pk = B < kOwn ? X.own[B][q] : X.pv[B][q];
+                float pk;
+                if constexpr (B < kOwn) pk = X.own[B][q];
+                else pk = X.pv[B][q];
                 X.acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(X.mo[B % (MA + 1)][t][q], pk, X.acc[t], 0, 0, 0);
             }
         };
@@ -975,6 +995,7 @@ struct DmaChain {
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * T, 0);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (B + 1 < E) blocks<B + 1, E>(X, L);
+      }
     }
 
     // Step s (LSX = s % HR selects the H register slot).  Barrier; operand
@@ -1000,7 +1021,7 @@ struct DmaChain {
         X.cur = lds + (s & 1) * (kTileV * LS);
         X.st = lds + S::STATE_FLOATS + (s & 1) * STAGE + (DIR == QLA_DIR_FWD ? L.a0 * K : 0);
 #pragma unroll
-        for (int b = 0; b < MA; ++b)
+        for (int b = 0; b < kFirstReads; ++b)
 #pragma unroll
             for (int t = 0; t < T; ++t) X.mo[b][t] = rd(X.st, t, b, L, X.tofs);
         Tl::template read_pv<0, kOwn, BP>(X.pv, X.cur, L);
@@ -1049,7 +1070,7 @@ struct DmaChain {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = 4 * L.g + q;
-                X.tofs[q] = 4 * (r * K + 4 * ((col >> 2) ^ r) + (col & 3));
+                X.tofs[q] = 4 * (r * K + 4 * ((col >> 2) ^ (r & (SWZ - 1))) + (col & 3));
             }
         } else {
 #pragma unroll
@@ -1108,26 +1129,33 @@ __device__ __forceinline__ int xcd_logical_id(int b, int G)
     return base + (b >> 3);
 }
 
-template <int K, int LAYOUT, int DIR>
-struct Plain {
-    static constexpr int WAVES = QLA_WAVES(K, DIR == QLA_DIR_FWD);
-    using Tl = Tile<K, LAYOUT, DIR, WAVES>;
+// The general kernel: compute size 256, the caller's K in kp (PAD when kp < 256).
+template <int LAYOUT, int DIR, bool PAD>
+struct General {
+    static constexpr int WAVES = general_waves(DIR == QLA_DIR_FWD);
+    using Tl = Tile<256, LAYOUT, DIR, WAVES, PAD>;
 };
 
-template <int K, int LAYOUT, int DIR>
-__global__ __launch_bounds__(64 * QLA_WAVES(K, DIR == QLA_DIR_FWD)) void correct_h0_kernel(
-    const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles)
+template <int LAYOUT, int DIR, bool PAD>
+__global__ __launch_bounds__(64 * general_waves(DIR == QLA_DIR_FWD)) void correct_h0_kernel(
+    const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles, int kp)
 {
-    using Tl = typename Plain<K, LAYOUT, DIR>::Tl;
+    using Tl = typename General<LAYOUT, DIR, PAD>::Tl;
     __shared__ __attribute__((aligned(16))) float lds[Tl::LDS_FLOATS];
     const int id = xcd_logical_id(blockIdx.x, gridDim.x);
     const int chain = id / tiles;
     const int tile = id - chain * tiles;
-    Tl::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds);
+    Tl::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds, kp);
+}
+
+template <int K>
+constexpr int dma_threads()
+{
+    return 64 * (K / 16 + kProducers);
 }
 
 template <int K, int LAYOUT>
-__global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void correct_h0_fwd_dma_kernel(
+__global__ __launch_bounds__(dma_threads<K>()) void correct_h0_fwd_dma_kernel(
     const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles)
 {
     using D = DmaChain<K, LAYOUT>;
@@ -1139,7 +1167,7 @@ __global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void cor
 }
 
 template <int K, int LAYOUT>
-__global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void correct_h0_bwd_dma_kernel(
+__global__ __launch_bounds__(dma_threads<K>()) void correct_h0_bwd_dma_kernel(
     const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles)
 {
     using D = DmaChain<K, LAYOUT, QLA_DIR_BWD>;
@@ -1153,34 +1181,35 @@ __global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void cor
 // Variable-length chains: sequence b has offs[b+1] - offs[b] segments; its
 // block of H / M / out starts at segment heads * offs[b] and holds its heads'
 // chains back to back, so chain (b, h) starts at segment heads * offs[b] +
-// h * n_b.  S0 is [n_seqs][heads][K][V] as usual.
-template <typename Chain, int K>
+// h * n_b.  S0 is [n_seqs][heads][K][V] as usual; kk is the caller's K.
+template <typename Chain>
 __device__ __forceinline__ Chain varlen_chain(const float* H, const float* M, float* out, int heads, int V, int chain,
-                                              const SeqTable& seqs)
+                                              const SeqTable& seqs, int kk)
 {
     const int b = chain / heads, h = chain - b * heads;
     const int n = seqs.offs[b + 1] - seqs.offs[b];
     const size_t base = (size_t)heads * seqs.offs[b] + (size_t)h * n;  // in segments
-    const size_t state = (size_t)K * V;
-    return Chain{M + base * K * K, H + base * state, out + base * state, n};
+    const size_t state = (size_t)kk * V;
+    return Chain{M + base * kk * kk, H + base * state, out + base * state, n};
 }
 
-template <int K, int LAYOUT, int DIR>
-__global__ __launch_bounds__(64 * QLA_WAVES(K, DIR == QLA_DIR_FWD)) void correct_h0_varlen_kernel(
-    const float* H, const float* __restrict__ M, const float* S0, float* out, int heads, int V, int tiles,
+template <int LAYOUT, int DIR, bool PAD>
+__global__ __launch_bounds__(64 * general_waves(DIR == QLA_DIR_FWD)) void correct_h0_varlen_kernel(
+    const float* H, const float* __restrict__ M, const float* S0, float* out, int heads, int V, int tiles, int kp,
     SeqTable seqs)
 {
-    using Tl = typename Plain<K, LAYOUT, DIR>::Tl;
+    using Tl = typename General<LAYOUT, DIR, PAD>::Tl;
     __shared__ __attribute__((aligned(16))) float lds[Tl::LDS_FLOATS];
     const int id = xcd_logical_id(blockIdx.x, gridDim.x);
     const int chain = id / tiles;
     const int tile = id - chain * tiles;
-    const auto C = varlen_chain<typename Tl::Chain, K>(H, M, out, heads, V, chain, seqs);
-    Tl::run_chain(C, S0 ? S0 + (size_t)chain * K * V : nullptr, V, tile, lds);
+    const int kk = PAD ? kp : 256;
+    const auto C = varlen_chain<typename Tl::Chain>(H, M, out, heads, V, chain, seqs, kk);
+    Tl::run_chain(C, S0 ? S0 + (size_t)chain * kk * V : nullptr, V, tile, lds, kp);
 }
 
 template <int K, int LAYOUT>
-__global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void correct_h0_fwd_dma_varlen_kernel(
+__global__ __launch_bounds__(dma_threads<K>()) void correct_h0_fwd_dma_varlen_kernel(
     const float* H, const float* __restrict__ M, const float* S0, float* out, int heads, int V, int tiles,
     SeqTable seqs)
 {
@@ -1189,12 +1218,12 @@ __global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void cor
     const int id = xcd_logical_id(blockIdx.x, gridDim.x);
     const int chain = id / tiles;
     const int tile = id - chain * tiles;
-    const auto C = varlen_chain<typename D::Chain, K>(H, M, out, heads, V, chain, seqs);
+    const auto C = varlen_chain<typename D::Chain>(H, M, out, heads, V, chain, seqs, K);
     D::run_chain(C, S0 ? S0 + (size_t)chain * K * V : nullptr, V, tile, lds);
 }
 
 template <int K, int LAYOUT>
-__global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void correct_h0_bwd_dma_varlen_kernel(
+__global__ __launch_bounds__(dma_threads<K>()) void correct_h0_bwd_dma_varlen_kernel(
     const float* H, const float* __restrict__ M, const float* S0, float* out, int heads, int V, int tiles,
     SeqTable seqs)
 {
@@ -1203,19 +1232,18 @@ __global__ __launch_bounds__(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)) void cor
     const int id = xcd_logical_id(blockIdx.x, gridDim.x);
     const int chain = id / tiles;
     const int tile = id - chain * tiles;
-    const auto C = varlen_chain<typename D::Chain, K>(H, M, out, heads, V, chain, seqs);
+    const auto C = varlen_chain<typename D::Chain>(H, M, out, heads, V, chain, seqs, K);
     D::run_chain(C, S0 ? S0 + (size_t)chain * K * V : nullptr, V, tile, lds);
 }
 
 // One grouped launch: each workgroup looks up its head's (layout, direction)
-// and runs that variant.  At K <= 128 the variants are the producer kernel's
-// (every variant has the same block shape and LDS size there); at K = 256
-// the general kernel's, with one wave count for all four.
-template <int K>
+// and runs that variant.  K <= 128: the producer kernel's variants (every
+// variant has the same block shape and LDS size there).  K > 128: the general
+// kernel's at compute size 256, with one wave count for all four.
+template <int K, bool PAD = false>
 struct Grouped {
-    static constexpr bool kDma = QLA_FWD_DMA && QLA_BWD_DMA && K <= 128;
-    static constexpr int WAVES = kDma ? QLA_WAVES(K, true) + QLA_DMA_WAVES : QLA_GROUPED_WAVES(K);
-    static constexpr int W = QLA_GROUPED_WAVES(K);
+    static constexpr bool kDma = K <= 128;
+    static constexpr int WAVES = kDma ? K / 16 + kProducers : kGroupedWaves;
     static constexpr int max2(int a, int b) { return a > b ? a : b; }
     static constexpr int lds_floats()
     {
@@ -1225,24 +1253,31 @@ struct Grouped {
                         max2(DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_FWD>::LDS_FLOATS,
                              DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_BWD>::LDS_FLOATS));
         else
-            return max2(Tile<K, QLA_LAYOUT_KV, QLA_DIR_FWD, W>::LDS_FLOATS, Tile<K, QLA_LAYOUT_KV, QLA_DIR_BWD, W>::LDS_FLOATS);
+            return max2(Tile<K, QLA_LAYOUT_KV, QLA_DIR_FWD, kGroupedWaves, PAD>::LDS_FLOATS,
+                        Tile<K, QLA_LAYOUT_KV, QLA_DIR_BWD, kGroupedWaves, PAD>::LDS_FLOATS);
     }
     static constexpr int LDS_FLOATS = lds_floats();
     template <int LAYOUT, int DIR>
     static __device__ __forceinline__ void run(const float* H, const float* M, const float* S0, float* out, int n_seg,
-                                               int V, size_t chain, int tile, float* lds)
+                                               int V, size_t chain, int tile, float* lds, int kp)
     {
         if constexpr (kDma) DmaChain<K, LAYOUT, DIR>::run(H, M, S0, out, n_seg, V, chain, tile, lds);
-        else Tile<K, LAYOUT, DIR, W>::run(H, M, S0, out, n_seg, V, chain, tile, lds);
+        else Tile<K, LAYOUT, DIR, kGroupedWaves, PAD>::run(H, M, S0, out, n_seg, V, chain, tile, lds, kp);
     }
 };
 
-template <int K>
-__global__ __launch_bounds__(64 * Grouped<K>::WAVES) void correct_h0_grouped_kernel(
-    const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles, int heads,
-    GroupTable table)
+template <int K, bool PAD>
+constexpr int grouped_threads()
 {
-    using G = Grouped<K>;
+    return 64 * Grouped<K, PAD>::WAVES;
+}
+
+template <int K, bool PAD>
+__global__ __launch_bounds__((grouped_threads<K, PAD>())) void correct_h0_grouped_kernel(
+    const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles, int heads,
+    int kp, GroupTable table)
+{
+    using G = Grouped<K, PAD>;
     __shared__ __attribute__((aligned(16))) float lds[G::LDS_FLOATS];
     const int id = xcd_logical_id(blockIdx.x, gridDim.x);
     const int chain = id / tiles;
@@ -1252,114 +1287,123 @@ __global__ __launch_bounds__(64 * Grouped<K>::WAVES) void correct_h0_grouped_ker
     for (int i = 0; i < table.n; ++i)
         if (head >= table.begin[i] && head < table.begin[i] + table.count[i]) variant = table.variant[i];
     switch (variant) {
-    case 0: G::template run<QLA_LAYOUT_KV, QLA_DIR_FWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
-    case 1: G::template run<QLA_LAYOUT_KV, QLA_DIR_BWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
-    case 2: G::template run<QLA_LAYOUT_VK, QLA_DIR_FWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
-    default: G::template run<QLA_LAYOUT_VK, QLA_DIR_BWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
+    case 0: G::template run<QLA_LAYOUT_KV, QLA_DIR_FWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds, kp); break;
+    case 1: G::template run<QLA_LAYOUT_KV, QLA_DIR_BWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds, kp); break;
+    case 2: G::template run<QLA_LAYOUT_VK, QLA_DIR_FWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds, kp); break;
+    default: G::template run<QLA_LAYOUT_VK, QLA_DIR_BWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds, kp); break;
     }
 }
 
+// ---- launchers ------------------------------------------------------------
 template <int K, int LAYOUT, int DIR>
-hipError_t launch_one(const LaunchArgs& a)
+hipError_t launch_dma(const LaunchArgs& a, dim3 grid, int tiles)
 {
-    const int tiles = (a.V + kTileV - 1) / kTileV;
-    const dim3 grid((unsigned)(a.chains * tiles));
-    if constexpr (QLA_FWD_DMA && DIR == QLA_DIR_FWD && K <= 128) {
-        hipLaunchKernelGGL((correct_h0_fwd_dma_kernel<K, LAYOUT>), grid, dim3(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)),
-                           0, (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles);
-    } else if constexpr (QLA_BWD_DMA && DIR == QLA_DIR_BWD && K <= 128) {
-        hipLaunchKernelGGL((correct_h0_bwd_dma_kernel<K, LAYOUT>), grid, dim3(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)),
-                           0, (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles);
-    } else {
-        hipLaunchKernelGGL((correct_h0_kernel<K, LAYOUT, DIR>), grid, dim3(64 * Plain<K, LAYOUT, DIR>::WAVES), 0,
+    if constexpr (DIR == QLA_DIR_FWD)
+        hipLaunchKernelGGL((correct_h0_fwd_dma_kernel<K, LAYOUT>), grid, dim3(dma_threads<K>()), 0,
                            (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles);
-    }
+    else
+        hipLaunchKernelGGL((correct_h0_bwd_dma_kernel<K, LAYOUT>), grid, dim3(dma_threads<K>()), 0,
+                           (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles);
     return hipGetLastError();
-}
-
-template <int K>
-hipError_t launch_k(const LaunchArgs& a)
-{
-    if (a.layout == QLA_LAYOUT_KV)
-        return a.direction == QLA_DIR_FWD ? launch_one<K, QLA_LAYOUT_KV, QLA_DIR_FWD>(a)
-                                          : launch_one<K, QLA_LAYOUT_KV, QLA_DIR_BWD>(a);
-    return a.direction == QLA_DIR_FWD ? launch_one<K, QLA_LAYOUT_VK, QLA_DIR_FWD>(a)
-                                      : launch_one<K, QLA_LAYOUT_VK, QLA_DIR_BWD>(a);
 }
 
 template <int K, int LAYOUT, int DIR>
-hipError_t launch_varlen_one(const LaunchArgs& a, const SeqTable& seqs)
+hipError_t launch_dma_varlen(const LaunchArgs& a, dim3 grid, int tiles, const SeqTable& seqs)
+{
+    if constexpr (DIR == QLA_DIR_FWD)
+        hipLaunchKernelGGL((correct_h0_fwd_dma_varlen_kernel<K, LAYOUT>), grid, dim3(dma_threads<K>()), 0,
+                           (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.heads, a.V, tiles, seqs);
+    else
+        hipLaunchKernelGGL((correct_h0_bwd_dma_varlen_kernel<K, LAYOUT>), grid, dim3(dma_threads<K>()), 0,
+                           (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.heads, a.V, tiles, seqs);
+    return hipGetLastError();
+}
+
+// kind: 0 plain, 1 variable-length, 2 grouped.
+template <int K, int LAYOUT, int DIR>
+hipError_t launch_k(const LaunchArgs& a, int kind, const SeqTable* seqs, const GroupTable* table)
 {
     const int tiles = (a.V + kTileV - 1) / kTileV;
     const dim3 grid((unsigned)(a.chains * tiles));
-    if constexpr (QLA_FWD_DMA && DIR == QLA_DIR_FWD && K <= 128) {
-        hipLaunchKernelGGL((correct_h0_fwd_dma_varlen_kernel<K, LAYOUT>), grid,
-                           dim3(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)), 0, (hipStream_t)a.stream, a.H, a.M, a.S0,
-                           a.out, a.heads, a.V, tiles, seqs);
-    } else if constexpr (QLA_BWD_DMA && DIR == QLA_DIR_BWD && K <= 128) {
-        hipLaunchKernelGGL((correct_h0_bwd_dma_varlen_kernel<K, LAYOUT>), grid,
-                           dim3(64 * (QLA_WAVES(K, true) + QLA_DMA_WAVES)), 0, (hipStream_t)a.stream, a.H, a.M, a.S0,
-                           a.out, a.heads, a.V, tiles, seqs);
+    if constexpr (K <= 128) {
+        if (kind == 2) {
+            hipLaunchKernelGGL((correct_h0_grouped_kernel<K, false>), grid, dim3(64 * Grouped<K>::WAVES), 0,
+                               (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles, a.heads, K, *table);
+            return hipGetLastError();
+        }
+        return kind == 1 ? launch_dma_varlen<K, LAYOUT, DIR>(a, grid, tiles, *seqs)
+                         : launch_dma<K, LAYOUT, DIR>(a, grid, tiles);
     } else {
-        hipLaunchKernelGGL((correct_h0_varlen_kernel<K, LAYOUT, DIR>), grid, dim3(64 * Plain<K, LAYOUT, DIR>::WAVES),
-                           0, (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.heads, a.V, tiles, seqs);
+        // K == 256: exact; 128 < a.K < 256: zero-padded to 256.
+        constexpr bool PAD = K != 256;
+        const int threads = 64 * general_waves(DIR == QLA_DIR_FWD);
+        if (kind == 2) {
+            hipLaunchKernelGGL((correct_h0_grouped_kernel<256, PAD>), grid, dim3(64 * Grouped<256, PAD>::WAVES), 0,
+                               (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles, a.heads, a.K,
+                               *table);
+        } else if (kind == 1) {
+            hipLaunchKernelGGL((correct_h0_varlen_kernel<LAYOUT, DIR, PAD>), grid, dim3(threads), 0,
+                               (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.heads, a.V, tiles, a.K, *seqs);
+        } else {
+            hipLaunchKernelGGL((correct_h0_kernel<LAYOUT, DIR, PAD>), grid, dim3(threads), 0, (hipStream_t)a.stream,
+                               a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles, a.K);
+        }
+        return hipGetLastError();
     }
-    return hipGetLastError();
 }
 
 template <int K>
-hipError_t launch_varlen_k(const LaunchArgs& a, const SeqTable& seqs)
+hipError_t launch_layout_dir(const LaunchArgs& a, int layout, int direction, int kind, const SeqTable* seqs,
+                             const GroupTable* table)
 {
-    if (a.layout == QLA_LAYOUT_KV)
-        return a.direction == QLA_DIR_FWD ? launch_varlen_one<K, QLA_LAYOUT_KV, QLA_DIR_FWD>(a, seqs)
-                                          : launch_varlen_one<K, QLA_LAYOUT_KV, QLA_DIR_BWD>(a, seqs);
-    return a.direction == QLA_DIR_FWD ? launch_varlen_one<K, QLA_LAYOUT_VK, QLA_DIR_FWD>(a, seqs)
-                                      : launch_varlen_one<K, QLA_LAYOUT_VK, QLA_DIR_BWD>(a, seqs);
+    if (layout == QLA_LAYOUT_KV)
+        return direction == QLA_DIR_FWD ? launch_k<K, QLA_LAYOUT_KV, QLA_DIR_FWD>(a, kind, seqs, table)
+                                        : launch_k<K, QLA_LAYOUT_KV, QLA_DIR_BWD>(a, kind, seqs, table);
+    return direction == QLA_DIR_FWD ? launch_k<K, QLA_LAYOUT_VK, QLA_DIR_FWD>(a, kind, seqs, table)
+                                    : launch_k<K, QLA_LAYOUT_VK, QLA_DIR_BWD>(a, kind, seqs, table);
 }
 
-template <int K>
-hipError_t launch_grouped_k(const LaunchArgs& a, const GroupTable& table)
+// The compiled kernel family for the caller's K (a multiple of 16 in [16, 256]).
+hipError_t dispatch(const LaunchArgs& a, int layout, int direction, int kind, const SeqTable* seqs,
+                    const GroupTable* table)
 {
-    const int tiles = (a.V + kTileV - 1) / kTileV;
-    const dim3 grid((unsigned)(a.chains * tiles));
-    hipLaunchKernelGGL((correct_h0_grouped_kernel<K>), grid, dim3(64 * Grouped<K>::WAVES), 0, (hipStream_t)a.stream,
-                       a.H, a.M,
-                       a.S0, a.out, a.n_seg, a.V, tiles, a.heads, table);
-    return hipGetLastError();
+    switch (a.K) {
+    case 16: return launch_layout_dir<16>(a, layout, direction, kind, seqs, table);
+    case 32: return launch_layout_dir<32>(a, layout, direction, kind, seqs, table);
+    case 48: return launch_layout_dir<48>(a, layout, direction, kind, seqs, table);
+    case 64: return launch_layout_dir<64>(a, layout, direction, kind, seqs, table);
+    case 80: return launch_layout_dir<80>(a, layout, direction, kind, seqs, table);
+    case 96: return launch_layout_dir<96>(a, layout, direction, kind, seqs, table);
+    case 112: return launch_layout_dir<112>(a, layout, direction, kind, seqs, table);
+    case 128: return launch_layout_dir<128>(a, layout, direction, kind, seqs, table);
+    case 256: return launch_layout_dir<256>(a, layout, direction, kind, seqs, table);
+    default:
+        if (a.K > 128 && a.K < 256 && a.K % 16 == 0) return launch_layout_dir<255>(a, layout, direction, kind, seqs, table);
+        return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 int tiles_for(int V) { return (V + kTileV - 1) / kTileV; }
 
+int max_threads_per_group() { return dma_threads<128>() > 64 * kGroupedWaves ? dma_threads<128>() : 64 * kGroupedWaves; }
+
 hipError_t launch_correct_h0(const LaunchArgs& a)
 {
-    switch (a.K) {
-    case 64: return launch_k<64>(a);
-    case 128: return launch_k<128>(a);
-    case 256: return launch_k<256>(a);
-    default: return hipErrorInvalidValue;
-    }
+    return dispatch(a, a.layout, a.direction, 0, nullptr, nullptr);
 }
 
 hipError_t launch_correct_h0_varlen(const LaunchArgs& a, const SeqTable& seqs)
 {
-    switch (a.K) {
-    case 64: return launch_varlen_k<64>(a, seqs);
-    case 128: return launch_varlen_k<128>(a, seqs);
-    case 256: return launch_varlen_k<256>(a, seqs);
-    default: return hipErrorInvalidValue;
-    }
+    return dispatch(a, a.layout, a.direction, 1, &seqs, nullptr);
 }
 
 hipError_t launch_correct_h0_grouped(const LaunchArgs& a, const GroupTable& table)
 {
-    switch (a.K) {
-    case 64: return launch_grouped_k<64>(a, table);
-    case 128: return launch_grouped_k<128>(a, table);
-    case 256: return launch_grouped_k<256>(a, table);
-    default: return hipErrorInvalidValue;
-    }
+    // The variant is chosen per head inside the kernel; layout/direction here
+    // only select a template instance, which the grouped launch ignores.
+    return dispatch(a, QLA_LAYOUT_KV, QLA_DIR_FWD, 2, nullptr, &table);
 }
 
 }  // namespace qla

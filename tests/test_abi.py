@@ -64,9 +64,12 @@ def test_enum_errors(lib):
     assert call(direction=-1) == -2
 
 
-@pytest.mark.parametrize("kw", [dict(K=96), dict(K=32), dict(V=6), dict(V=0), dict(V=4100),
+@pytest.mark.parametrize("kw", [dict(K=0), dict(K=8), dict(K=100), dict(K=264), dict(K=272), dict(K=-16),
+                                dict(V=6), dict(V=0), dict(V=4100),
                                 dict(batch=-1), dict(heads=-2), dict(n_seg=-1),
-                                dict(batch=2 ** 30, heads=2 ** 10)])
+                                dict(batch=2 ** 30, heads=2 ** 10),
+                                # 2^23 workgroups fit an int, but not their work-items a 32-bit count
+                                dict(batch=2 ** 23, heads=1, V=16)])
 def test_shape_errors(lib, kw):
     assert call(**kw) == -3
 
@@ -136,7 +139,7 @@ def test_group_empty_call_ok(lib):
 
 def test_binding_raises_with_status(lib):
     with pytest.raises(qla.QlaError) as e:
-        qla.qla_correct_h0(A, A + 0x10000000, None, A + 0x20000000, 0, 0, 1, 1, 1, 96, 64, stream=0)
+        qla.qla_correct_h0(A, A + 0x10000000, None, A + 0x20000000, 0, 0, 1, 1, 1, 100, 64, stream=0)
     assert e.value.status == -3
 
 
@@ -161,7 +164,7 @@ def test_varlen_offset_errors(lib, offs, n_seqs):
 def test_varlen_enum_and_shape_errors(lib):
     assert varlen_call([0, 2], layout=2) == -2
     assert varlen_call([0, 2], direction=5) == -2
-    assert varlen_call([0, 2], K=96) == -3
+    assert varlen_call([0, 2], K=100) == -3
     assert varlen_call([0, 2], heads=-1) == -3
     assert varlen_call([0, 2 ** 28], heads=16) == -3       # heads * total > INT32_MAX
 

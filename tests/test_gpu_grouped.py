@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 GROUPS = [(0, 1, "vk", "bwd"), (1, 2, "kv", "fwd"), (3, 3, "vk", "fwd"), (6, 1, "kv", "bwd")]
 
 
-@pytest.mark.parametrize("K", [64, 128, 256])
+@pytest.mark.parametrize("K", [16, 48, 64, 96, 128, 160, 224, 256])
 @pytest.mark.parametrize("with_s0", [True, False])
 def test_grouped_uneven(K, with_s0):
     import torch
@@ -66,7 +66,7 @@ def test_grouped_in_place():
     assert torch.equal(Hd.view(torch.int32), sep.view(torch.int32))
 
 
-@pytest.mark.parametrize("K", [64, 128])
+@pytest.mark.parametrize("K", [32, 64, 112, 128])
 def test_grouped_matches_plain_calls_bitwise(K):
     """At K <= 128 a grouped call runs the same per-chain code as plain calls:
     every group's output equals, bit for bit, a plain call on that group's heads."""

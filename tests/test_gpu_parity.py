@@ -14,6 +14,9 @@ from gpu_util import assert_parity, bits, decode_mismatch, lay, run_hip
 pytestmark = pytest.mark.gpu
 
 VARIANTS = [("kv", "fwd"), ("kv", "bwd"), ("vk", "fwd"), ("vk", "bwd")]
+# every head dimension the library accepts: K <= 128 runs the producer kernels
+# with K/16 MFMA waves, 128 < K < 256 the general kernel zero-padded to 256
+ALL_K = list(range(16, 257, 16))
 
 
 def _ragged_v(K):
@@ -21,7 +24,7 @@ def _ragged_v(K):
     return K + 20
 
 
-@pytest.mark.parametrize("K", [64, 128, 256])
+@pytest.mark.parametrize("K", ALL_K)
 @pytest.mark.parametrize("layout,direction", VARIANTS)
 @pytest.mark.parametrize("with_s0", [True, False])
 def test_random_small(K, layout, direction, with_s0):
@@ -32,7 +35,7 @@ def test_random_small(K, layout, direction, with_s0):
     assert_parity(got, ref, f"K={K} V={V} {layout} {direction}")
 
 
-@pytest.mark.parametrize("K", [64, 128, 256])
+@pytest.mark.parametrize("K", ALL_K)
 @pytest.mark.parametrize("layout,direction", VARIANTS)
 def test_signed_permutation_bit_exact(K, layout, direction):
     """Every fp32 product and sum is an exact small integer: GPU == oracle bit for bit."""
@@ -48,7 +51,9 @@ def test_signed_permutation_bit_exact(K, layout, direction):
     assert np.array_equal(bits(got), bits(want)), decode_mismatch(got, want)
 
 
-@pytest.mark.parametrize("K,V,n", [(64, 64, 12), (128, 128, 8), (256, 256, 16), (128, 84, 5)])
+@pytest.mark.parametrize("K,V,n", [(64, 64, 12), (128, 128, 8), (256, 256, 16), (128, 84, 5), (16, 16, 5),
+                                   (48, 100, 7), (96, 40, 4), (112, 112, 6), (160, 160, 3), (192, 36, 4),
+                                   (240, 240, 2)])
 @pytest.mark.parametrize("layout,direction", VARIANTS)
 def test_coded_sentinel_m_zero(K, V, n, layout, direction):
     """M = 0 and coded H: out must equal H exactly; a mismatch names the segment read."""
@@ -129,3 +134,26 @@ def test_many_chains():
         ref = oracle.correct_h0(lay(H, layout), M, lay(S0, layout), layout, direction)
         got = run_hip(lay(H, layout), M, lay(S0, layout), layout, direction).cpu().numpy()
         assert_parity(got, ref, f"5000 chains {layout} {direction}")
+
+
+def test_binding_rejects_tensors_the_library_cannot_check():
+    """An undersized view of a larger allocation, a bf16 tensor and a transposed
+    view all pass the library's allocation-extent check; the binding refuses them."""
+    import torch
+
+    import linear_attention_context_amd as qla
+    B, NH, N, K, V = 1, 2, 3, 64, 64
+    big = torch.zeros(4 * B * NH * N * K * max(K, V), device="cuda")
+    need = B * NH * N * K * V
+    H = big[:need]
+    M = big[need:need + B * NH * N * K * K]
+    out = torch.empty(need, device="cuda")
+    assert qla.raw_correct_h0(H, M, None, out, "kv", "fwd", B, NH, N, K, V) == 0
+    torch.cuda.synchronize()
+    assert qla.raw_correct_h0(H[:-1], M, None, out, "kv", "fwd", B, NH, N, K, V) == qla.QLA_ERR_MEMORY
+    assert qla.raw_correct_h0(H, M[:-16], None, out, "kv", "fwd", B, NH, N, K, V) == qla.QLA_ERR_MEMORY
+    assert qla.raw_correct_h0(H.bfloat16(), M, None, out, "kv", "fwd", B, NH, N, K, V) == qla.QLA_ERR_MEMORY
+    Ht = H.view(B * NH * N, K, V).transpose(-1, -2)
+    assert qla.raw_correct_h0(Ht, M, None, out, "kv", "fwd", B, NH, N, K, V) == qla.QLA_ERR_MEMORY
+    with pytest.raises(qla.QlaError):
+        qla.qla_correct_h0(H, M, big[:K * V - 4], out, "kv", "fwd", B, NH, N, K, V)

@@ -1,5 +1,5 @@
 """GPU parity of qla_correct_h0_varlen: ragged chains (including empty ones) in
-the packed layout, every variant, K = 64 / 128 / 256, with and without S0,
+the packed layout, every variant, K = 48 / 64 / 96 / 128 / 192 / 256, with and without S0,
 against the fp64 oracle on every state; equal lengths give the bits of the
 fixed-length entry point; in place; the all-empty call writes nothing."""
 import numpy as np
@@ -32,6 +32,9 @@ def run_varlen(H, M, S0, offs, heads, layout, direction, K, V, in_place=False):
     (128, 128, 3, [0, 7, 2, 12]),
     (128, 80, 2, [4, 1, 0, 0, 6]),     # ragged V tail: 16-column tiles over 80
     (256, 256, 2, [3, 0, 6]),
+    (48, 52, 3, [2, 5, 0, 1]),         # K = 48: three MFMA waves, uneven producer shares
+    (96, 96, 2, [3, 0, 4]),
+    (192, 100, 2, [2, 5]),             # zero-padded to the K = 256 kernel
 ])
 @pytest.mark.parametrize("with_s0", [True, False])
 def test_varlen_parity(K, V, heads, seg_counts, with_s0):
