@@ -90,3 +90,30 @@ def decode_mismatch(got, want, n_show=5):
             msg += f" (value is segment {seg} row {r} col {c}; expected segment {idx[-3]})"
         msgs.append(msg)
     return f"{len(bad)} mismatches; " + "; ".join(msgs)
+
+
+def oracle_threaded(H, M, S0, layout, direction, threads=None):
+    """The fp64 oracle over all chains of (H, M, S0), the chains split across
+    host threads (its C loops release the interpreter lock).  Leading axes of H
+    and M are the chains; the result is shaped like H."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    lead = H.shape[:-3]
+    chains = int(np.prod(lead)) if lead else 1
+    Hf = H.reshape((chains,) + H.shape[-3:])
+    Mf = M.reshape((chains,) + M.shape[-3:])
+    Sf = None if S0 is None else S0.reshape((chains,) + S0.shape[-2:])
+    threads = threads or max(1, min(16, len(os.sched_getaffinity(0))))
+    bounds = [chains * i // threads for i in range(threads + 1)]
+    out = np.empty(Hf.shape, np.float64)
+
+    def part(i):
+        lo, hi = bounds[i], bounds[i + 1]
+        if hi > lo:
+            out[lo:hi] = oracle.correct_h0(Hf[lo:hi], Mf[lo:hi], None if Sf is None else Sf[lo:hi], layout, direction)
+
+    with ThreadPoolExecutor(threads) as pool:
+        list(pool.map(part, range(threads)))
+    return out.reshape(H.shape)
