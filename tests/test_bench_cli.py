@@ -22,10 +22,31 @@ def test_more_than_one_gpu_exits_with_message():
 
 
 def test_kernel_names():
+    """The names rocprofv3 reports for the kernels each variant launches."""
     assert bench.kernel_name("kv_fwd", 128) == "correct_h0_fwd_dma_kernel<128, 0>"
     assert bench.kernel_name("vk_fwd", 64) == "correct_h0_fwd_dma_kernel<64, 1>"
-    assert bench.kernel_name("vk_bwd", 128) == "correct_h0_kernel<128, 1, 1>"
-    assert bench.kernel_name("kv_fwd", 256) == "correct_h0_kernel<256, 0, 0>"
+    assert bench.kernel_name("vk_bwd", 128) == "correct_h0_bwd_dma_kernel<128, 1>"
+    assert bench.kernel_name("kv_bwd", 48) == "correct_h0_bwd_dma_kernel<48, 0>"
+    assert bench.kernel_name("kv_fwd", 256) == "correct_h0_kernel<0, 0, false>"
+    assert bench.kernel_name("vk_bwd", 256) == "correct_h0_kernel<1, 1, false>"
+    assert bench.kernel_name("kv_bwd", 192) == "correct_h0_kernel<0, 1, true>"
+
+
+def test_kernel_names_match_the_built_library():
+    """Every name kernel_name() gives for the 32K x 32-head step and the wide
+    configuration is a kernel the built library contains (mangled)."""
+    import re
+    lib = os.path.join(ROOT, "linear_attention_context_amd", "libqla.so")
+    if not os.path.exists(lib):
+        pytest.skip("libqla.so is not built")
+    data = open(lib, "rb").read()
+    for v in ("kv_fwd", "vk_fwd", "kv_bwd", "vk_bwd"):
+        for K in (128, 256, 192):
+            name = bench.kernel_name(v, K)
+            base, targs = re.match(r"(\w+)<(.*)>", name).groups()
+            parts = [t.strip() for t in targs.split(",")]
+            mangled = "".join("Lb0E" if t == "false" else "Lb1E" if t == "true" else f"Li{t}E" for t in parts)
+            assert (base + "I" + mangled).encode() in data, name
 
 
 def test_source_hash_ignores_comments(tmp_path, monkeypatch):
