@@ -13,10 +13,11 @@ back, so every call streams its inputs from HBM.  The same calls on one
 resident set (warm) and the bandwidth of a plain 1 GiB device copy are
 reported beside it.
 
-Timing: --warmup untimed steps first (640 by default: calls on freshly
-allocated buffers keep getting faster for the first thousand or so calls
-over them), then each variant's calls of the timed steps back to back, with
-HIP events on the launch stream at the boundaries (--mode direct, default).
+Timing: untimed warm-up steps first (--warmup, and at least --warmup-seconds
+of back-to-back calls: a GPU that was idle runs at a low clock and needs tens
+of ms of continuous work to reach its working clock), then each variant's
+calls of the timed steps back to back, with HIP events on the launch stream at
+the boundaries (--mode direct, default).
 --mode graph follows the pages' protocol instead: each variant's launches are
 captured in hipGraphs of 16 calls and replayed.
 
@@ -61,6 +62,8 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=320)
     p.add_argument("--warmup", type=int, default=640)
+    p.add_argument("--warmup-seconds", type=float, default=0.3,
+                   help="warm up for at least this long (the GPU's clock ramps up over tens of ms of work)")
     p.add_argument("--mode", choices=("direct", "graph"), default="direct",
                    help="direct launches (default) or replays of captured hipGraphs")
     p.add_argument("--graph-calls", type=int, default=16, help="launches per captured graph (--mode graph)")
@@ -383,9 +386,18 @@ def main(argv=None):
         # Direct launches on the stream: each variant's K calls back to back
         # (same work as interleaving them), each run bracketed by HIP events on
         # the launch stream; rotating buffer sets.
-        for i in range(args.warmup):
+        # Warm-up: --warmup steps, and at least --warmup-seconds of back-to-back
+        # calls.  An idle GPU runs at a low clock and takes tens of ms of
+        # continuous work to reach its working clock; calls timed before that
+        # read 10-15% slow.
+        t_w = time.perf_counter()
+        i = 0
+        while i < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
             for v in names:
                 launch(v, i % args.rotate, stream.cuda_stream)
+            i += 1
+            if i % 64 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(nv + 1)]
         wall0 = time.perf_counter()

@@ -79,35 +79,40 @@ def qla_status_str(status: int, lib: ctypes.CDLL | None = None) -> str:
     return (lib or load_library()).qla_status_str(int(status)).decode()
 
 
-def _ptr(x):
+QLA_ERR_MEMORY = -8
+_BAD = object()   # a tensor argument the library must not see
+_F32 = None
+
+
+def _checked_ptr(x, need: int):
+    """Pointer of one buffer argument.  A tensor must be float32, contiguous and
+    hold at least ``need`` elements (the extent the call reads or writes);
+    otherwise ``_BAD``.  Integer addresses and None pass through: the library
+    checks those (that a pointer is device memory is always its check)."""
+    global _F32
     if x is None:
         return None
-    if isinstance(x, int):
+    if type(x) is int:
         return x
-    if hasattr(x, "data_ptr"):
+    if _F32 is None:
+        import torch
+        _F32 = torch.float32
+    try:
+        if x.dtype is not _F32 or not x.is_contiguous() or x.numel() < need:
+            return _BAD
         return x.data_ptr() or None
-    raise TypeError(f"expected a tensor, an int address or None, got {type(x)!r}")
+    except AttributeError:
+        raise TypeError(f"expected a tensor, an int address or None, got {type(x)!r}") from None
 
 
-QLA_ERR_MEMORY = -8
-
-
-def _tensor_ok(x, need: int) -> bool:
-    """A tensor argument must be float32, contiguous, on a GPU and hold at least
-    ``need`` elements (the extent the call reads or writes).  Integer
-    addresses and None are passed through unchecked: the library checks those."""
-    if x is None or isinstance(x, int) or not hasattr(x, "data_ptr"):
-        return True
-    import torch
-    return (x.dtype == torch.float32 and x.is_cuda and x.is_contiguous() and x.numel() >= need)
-
-
-def _extents_ok(H, M, S0, out, states: int, chains: int, K: int, V: int) -> bool:
-    """``states`` segment states of H / out (K*V floats each) and M (K*K), ``chains`` of S0."""
-    if states <= 0 or K <= 0 or V <= 0:
-        return True  # empty or malformed: the library decides
-    return (_tensor_ok(H, states * K * V) and _tensor_ok(out, states * K * V)
-            and _tensor_ok(M, states * K * K) and _tensor_ok(S0, chains * K * V))
+def _buffers(H, M, S0, out, states: int, chains: int, K: int, V: int):
+    """Pointers of (H, M, S0, out) for ``states`` segment states (K*V floats of
+    H and out, K*K of M each) and ``chains`` initial states, or None if a
+    tensor is unusable."""
+    kv = max(states * K * V, 0)
+    ptrs = (_checked_ptr(H, kv), _checked_ptr(M, max(states * K * K, 0)),
+            _checked_ptr(S0, max(chains * K * V, 0)), _checked_ptr(out, kv))
+    return None if _BAD in ptrs else ptrs
 
 
 def _stream(stream):
@@ -120,6 +125,8 @@ def _stream(stream):
 
 
 def _enum(value, names):
+    if type(value) is int:
+        return value
     if isinstance(value, str):
         return names[value]
     return int(value)
@@ -135,10 +142,10 @@ def raw_correct_h0(H, M, S0, out, layout, direction, batch, heads, n_seg, K, V, 
     without calling it if a tensor argument is not float32, contiguous, on the
     GPU and large enough)."""
     lib = lib or load_library()
-    if not _extents_ok(H, M, S0, out, batch * heads * n_seg, batch * heads, K, V):
+    p = _buffers(H, M, S0, out, batch * heads * n_seg, batch * heads, K, V)
+    if p is None:
         return QLA_ERR_MEMORY
-    return lib.qla_correct_h0(_ptr(H), _ptr(M), _ptr(S0), _ptr(out),
-                              _enum(layout, _LAYOUT_NAMES), _enum(direction, _DIR_NAMES),
+    return lib.qla_correct_h0(p[0], p[1], p[2], p[3], _enum(layout, _LAYOUT_NAMES), _enum(direction, _DIR_NAMES),
                               batch, heads, n_seg, K, V, _stream(stream))
 
 
@@ -163,12 +170,12 @@ def raw_correct_h0_grouped(H, M, S0, out, groups, batch, heads, n_seg, K, V, str
                            lib: ctypes.CDLL | None = None, n_groups: int | None = None) -> int:
     """Call qla_correct_h0_grouped; ``groups`` is a list of (head_begin, head_count, layout, direction)."""
     lib = lib or load_library()
-    if not _extents_ok(H, M, S0, out, batch * heads * n_seg, batch * heads, K, V):
+    p = _buffers(H, M, S0, out, batch * heads * n_seg, batch * heads, K, V)
+    if p is None:
         return QLA_ERR_MEMORY
     arr = _groups(groups)
     n = len(groups) if n_groups is None else n_groups
-    return lib.qla_correct_h0_grouped(_ptr(H), _ptr(M), _ptr(S0), _ptr(out), arr, n,
-                                      batch, heads, n_seg, K, V, _stream(stream))
+    return lib.qla_correct_h0_grouped(p[0], p[1], p[2], p[3], arr, n, batch, heads, n_seg, K, V, _stream(stream))
 
 
 def qla_correct_h0_grouped(H, M, S0, out, groups, batch, heads, n_seg, K, V, stream=None,
@@ -184,6 +191,7 @@ def raw_correct_h0_varlen(H, M, S0, out, layout, direction, seg_offsets, heads, 
     """Call qla_correct_h0_varlen; ``seg_offsets`` is a sequence of n_seqs + 1 ints
     (host memory), or None to pass a NULL pointer."""
     lib = lib or load_library()
+    states = chains = 0
     if seg_offsets is None:
         arr, n = None, (0 if n_seqs is None else n_seqs)
     else:
@@ -191,11 +199,13 @@ def raw_correct_h0_varlen(H, M, S0, out, layout, direction, seg_offsets, heads, 
         n = len(offs) - 1 if n_seqs is None else n_seqs
         # the library reads n + 1 offsets: never past the array (missing ones read as 0)
         arr = (ctypes.c_int * max(len(offs), n + 1, 1))(*offs)
-        if 0 <= n < len(offs) and not _extents_ok(H, M, S0, out, heads * offs[n], n * heads, K, V):
-            return QLA_ERR_MEMORY
-    return lib.qla_correct_h0_varlen(_ptr(H), _ptr(M), _ptr(S0), _ptr(out),
-                                     _enum(layout, _LAYOUT_NAMES), _enum(direction, _DIR_NAMES),
-                                     arr, n, heads, K, V, _stream(stream))
+        if 0 <= n < len(offs):
+            states, chains = heads * offs[n], n * heads
+    p = _buffers(H, M, S0, out, states, chains, K, V)
+    if p is None:
+        return QLA_ERR_MEMORY
+    return lib.qla_correct_h0_varlen(p[0], p[1], p[2], p[3], _enum(layout, _LAYOUT_NAMES),
+                                     _enum(direction, _DIR_NAMES), arr, n, heads, K, V, _stream(stream))
 
 
 def qla_correct_h0_varlen(H, M, S0, out, layout, direction, seg_offsets, heads, K, V, stream=None,

@@ -4,7 +4,8 @@ The C ABI sees raw pointers; under PyTorch's caching allocator the runtime's
 allocation extent is a whole cached segment, not the tensor, so a too-small
 view, a wrong dtype or a strided view would pass the library's own checks.
 The binding therefore checks every tensor argument first and returns
-QLA_ERR_MEMORY (-8) without calling the library.
+QLA_ERR_MEMORY (-8) without calling the library.  (Whether a pointer is
+device memory at all stays the library's check.)
 """
 import pytest
 import torch
@@ -15,8 +16,8 @@ import linear_attention_context_amd as qla
 class FakeTensor:
     """Stands in for a device tensor: only what the binding's checks read."""
 
-    def __init__(self, numel, dtype=torch.float32, cuda=True, contiguous=True, ptr=0x10000000):
-        self._n, self.dtype, self.is_cuda, self._c, self._p = numel, dtype, cuda, contiguous, ptr
+    def __init__(self, numel, dtype=torch.float32, contiguous=True, ptr=0x10000000):
+        self._n, self.dtype, self._c, self._p = numel, dtype, contiguous, ptr
 
     def numel(self):
         return self._n
@@ -58,7 +59,6 @@ def args(**kw):
     dict(H=FakeTensor(STATES * K * V, dtype=torch.bfloat16)),     # wrong dtype
     dict(M=FakeTensor(STATES * K * K, dtype=torch.float64)),
     dict(out=FakeTensor(STATES * K * V, contiguous=False)),       # a strided view
-    dict(S0=FakeTensor(B * NH * K * V, cuda=False)),              # host memory
 ])
 def test_rejected_before_the_library(bad):
     a = args(**bad)
