@@ -112,8 +112,10 @@ QLA_API int qla_correct_h0(const float* H, const float* M, const float* S0, floa
                    int K, int V, void* stream);
 
 /*
- * qla_correct_h0_grouped -- one launch over batch*heads chains whose layout and
- * direction vary by head group.  `groups` is a HOST array of n_groups entries
+ * qla_correct_h0_grouped -- one call over batch*heads chains whose layout and
+ * direction vary by head group: one launch at K <= 128; above, the forward
+ * groups and the backward groups are one launch each (the two directions use
+ * different block shapes there), both enqueued on `stream`.  `groups` is a HOST array of n_groups entries
  * (1 <= n_groups <= QLA_MAX_GROUPS) whose head ranges must partition
  * [0, heads) exactly; it is copied into the launch and may be freed on return.
  * Buffers are laid out as for qla_correct_h0, with each head's matrices in its

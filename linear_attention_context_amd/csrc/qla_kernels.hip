@@ -74,10 +74,9 @@ constexpr int kMoAhead = 2;    // general kernel: staged M operand reads run thi
 // (16 columns would halve that).  128 < K < 256 runs the same general kernel
 // at compute size 256 with the missing rows and columns read as zeros (a
 // zero-padded M and state give exactly the unpadded result in the first K
-// rows).  The grouped kernel at K > 128 has one block size for all its
-// groups and uses eight waves.
+// rows).  A grouped call at K > 128 runs its forward and its backward
+// groups as one launch each, with these same wave counts.
 constexpr int general_waves(bool fwd) { return fwd ? 8 : 4; }
-constexpr int kGroupedWaves = 8;
 // Prefetch distance of the general kernel, in units (64-k panels) of M.
 constexpr int kPrefetchUnits = 1;
 constexpr int pow2_divisor(int x) { return x % 2 ? 1 : 2 * pow2_divisor(x / 2); }
@@ -972,7 +971,10 @@ struct DmaChain {
     static __device__ __forceinline__ void blocks(Ctx& X, const Lane& L)
     {
       if constexpr (B < E) {
-        constexpr int nr = B + MA < BP ? T : 0;
+        // LDS read instructions of one staged operand block: one 16-byte read
+        // forward, four 4-byte reads backward (all placed after the block's
+        // second MFMA, so each has six MFMAs to land)
+        constexpr int nr = B + MA < BP ? T * (DIR == QLA_DIR_FWD ? 1 : 4) : 0;
         auto mfma = [&](int q) {
 #pragma unroll
             for (int t = 0; t < T; ++t) {
@@ -1236,49 +1238,32 @@ __global__ __launch_bounds__(dma_threads<K>()) void correct_h0_bwd_dma_varlen_ke
     D::run_chain(C, S0 ? S0 + (size_t)chain * K * V : nullptr, V, tile, lds);
 }
 
-// One grouped launch: each workgroup looks up its head's (layout, direction)
-// and runs that variant.  K <= 128: the producer kernel's variants (every
-// variant has the same block shape and LDS size there).  K > 128: the general
-// kernel's at compute size 256, with one wave count for all four.
-template <int K, bool PAD = false>
+// Grouped calls.  K <= 128: one launch; each workgroup looks up its head's
+// (layout, direction) and runs that variant of the producer kernel (every
+// variant has the same block shape and LDS size there).
+template <int K>
 struct Grouped {
-    static constexpr bool kDma = K <= 128;
-    static constexpr int WAVES = kDma ? K / 16 + kProducers : kGroupedWaves;
+    static_assert(K <= 128, "one grouped launch covers the producer kernels");
+    static constexpr int WAVES = K / 16 + kProducers;
     static constexpr int max2(int a, int b) { return a > b ? a : b; }
-    static constexpr int lds_floats()
-    {
-        if constexpr (kDma)
-            return max2(max2(DmaChain<K, QLA_LAYOUT_KV, QLA_DIR_FWD>::LDS_FLOATS,
-                             DmaChain<K, QLA_LAYOUT_KV, QLA_DIR_BWD>::LDS_FLOATS),
-                        max2(DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_FWD>::LDS_FLOATS,
-                             DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_BWD>::LDS_FLOATS));
-        else
-            return max2(Tile<K, QLA_LAYOUT_KV, QLA_DIR_FWD, kGroupedWaves, PAD>::LDS_FLOATS,
-                        Tile<K, QLA_LAYOUT_KV, QLA_DIR_BWD, kGroupedWaves, PAD>::LDS_FLOATS);
-    }
-    static constexpr int LDS_FLOATS = lds_floats();
-    template <int LAYOUT, int DIR>
-    static __device__ __forceinline__ void run(const float* H, const float* M, const float* S0, float* out, int n_seg,
-                                               int V, size_t chain, int tile, float* lds, int kp)
-    {
-        if constexpr (kDma) DmaChain<K, LAYOUT, DIR>::run(H, M, S0, out, n_seg, V, chain, tile, lds);
-        else Tile<K, LAYOUT, DIR, kGroupedWaves, PAD>::run(H, M, S0, out, n_seg, V, chain, tile, lds, kp);
-    }
+    static constexpr int LDS_FLOATS = max2(max2(DmaChain<K, QLA_LAYOUT_KV, QLA_DIR_FWD>::LDS_FLOATS,
+                                                DmaChain<K, QLA_LAYOUT_KV, QLA_DIR_BWD>::LDS_FLOATS),
+                                           max2(DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_FWD>::LDS_FLOATS,
+                                                DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_BWD>::LDS_FLOATS));
 };
 
-template <int K, bool PAD>
+template <int K>
 constexpr int grouped_threads()
 {
-    return 64 * Grouped<K, PAD>::WAVES;
+    return 64 * Grouped<K>::WAVES;
 }
 
-template <int K, bool PAD>
-__global__ __launch_bounds__((grouped_threads<K, PAD>())) void correct_h0_grouped_kernel(
+template <int K>
+__global__ __launch_bounds__((grouped_threads<K>())) void correct_h0_grouped_kernel(
     const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles, int heads,
-    int kp, GroupTable table)
+    GroupTable table)
 {
-    using G = Grouped<K, PAD>;
-    __shared__ __attribute__((aligned(16))) float lds[G::LDS_FLOATS];
+    __shared__ __attribute__((aligned(16))) float lds[Grouped<K>::LDS_FLOATS];
     const int id = xcd_logical_id(blockIdx.x, gridDim.x);
     const int chain = id / tiles;
     const int tile = id - chain * tiles;
@@ -1287,11 +1272,51 @@ __global__ __launch_bounds__((grouped_threads<K, PAD>())) void correct_h0_groupe
     for (int i = 0; i < table.n; ++i)
         if (head >= table.begin[i] && head < table.begin[i] + table.count[i]) variant = table.variant[i];
     switch (variant) {
-    case 0: G::template run<QLA_LAYOUT_KV, QLA_DIR_FWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds, kp); break;
-    case 1: G::template run<QLA_LAYOUT_KV, QLA_DIR_BWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds, kp); break;
-    case 2: G::template run<QLA_LAYOUT_VK, QLA_DIR_FWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds, kp); break;
-    default: G::template run<QLA_LAYOUT_VK, QLA_DIR_BWD>(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds, kp); break;
+    case 0: DmaChain<K, QLA_LAYOUT_KV, QLA_DIR_FWD>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
+    case 1: DmaChain<K, QLA_LAYOUT_KV, QLA_DIR_BWD>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
+    case 2: DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_FWD>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
+    default: DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_BWD>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
     }
+}
+
+// K > 128: the general kernel's backward block (four waves, a whole 128-byte
+// line per M row load) differs from its forward one (eight waves), so the
+// groups of one direction run as one launch, the other direction's as a
+// second.  `table` holds only this launch's groups, and the launch covers
+// batch x sel chains, sel = the heads in those groups: logical chain c is
+// batch entry c / sel and the (c % sel)-th head of the groups taken in table
+// order.
+template <int DIR, bool PAD>
+struct GroupedDir {
+    static constexpr int WAVES = general_waves(DIR == QLA_DIR_FWD);
+    using TK = Tile<256, QLA_LAYOUT_KV, DIR, WAVES, PAD>;
+    using TV = Tile<256, QLA_LAYOUT_VK, DIR, WAVES, PAD>;
+    static constexpr int LDS_FLOATS = TK::LDS_FLOATS > TV::LDS_FLOATS ? TK::LDS_FLOATS : TV::LDS_FLOATS;
+};
+
+template <int DIR, bool PAD>
+__global__ __launch_bounds__(64 * general_waves(DIR == QLA_DIR_FWD)) void correct_h0_grouped_dir_kernel(
+    const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles, int heads,
+    int kp, int sel, GroupTable table)
+{
+    using G = GroupedDir<DIR, PAD>;
+    __shared__ __attribute__((aligned(16))) float lds[G::LDS_FLOATS];
+    const int id = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int c = id / tiles;
+    const int tile = id - c * tiles;
+    const int b = c / sel;
+    int j = c - b * sel;
+    int head = 0, layout = QLA_LAYOUT_KV;
+    for (int i = 0; i < table.n; ++i) {
+        if (j >= 0 && j < table.count[i]) {
+            head = table.begin[i] + j;
+            layout = table.variant[i] >> 1;
+        }
+        j -= table.count[i];
+    }
+    const size_t chain = (size_t)b * heads + head;
+    if (layout == QLA_LAYOUT_KV) G::TK::run(H, M, S0, out, n_seg, V, chain, tile, lds, kp);
+    else G::TV::run(H, M, S0, out, n_seg, V, chain, tile, lds, kp);
 }
 
 // ---- launchers ------------------------------------------------------------
@@ -1319,6 +1344,29 @@ hipError_t launch_dma_varlen(const LaunchArgs& a, dim3 grid, int tiles, const Se
     return hipGetLastError();
 }
 
+// The groups of direction DIR of a grouped call at K > 128, as one launch
+// (none if the call has no such group).
+template <int DIR, bool PAD>
+hipError_t launch_grouped_dir(const LaunchArgs& a, int tiles, const GroupTable& all)
+{
+    GroupTable t{};
+    int sel = 0;
+    for (int i = 0; i < all.n; ++i) {
+        if ((all.variant[i] & 1) != DIR) continue;
+        t.begin[t.n] = all.begin[i];
+        t.count[t.n] = all.count[i];
+        t.variant[t.n] = all.variant[i];
+        sel += all.count[i];
+        ++t.n;
+    }
+    if (sel == 0) return hipSuccess;
+    const long long batch = a.chains / a.heads;
+    const dim3 grid((unsigned)(batch * sel * tiles));
+    hipLaunchKernelGGL((correct_h0_grouped_dir_kernel<DIR, PAD>), grid, dim3(64 * general_waves(DIR == QLA_DIR_FWD)),
+                       0, (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles, a.heads, a.K, sel, t);
+    return hipGetLastError();
+}
+
 // kind: 0 plain, 1 variable-length, 2 grouped.
 template <int K, int LAYOUT, int DIR>
 hipError_t launch_k(const LaunchArgs& a, int kind, const SeqTable* seqs, const GroupTable* table)
@@ -1327,8 +1375,8 @@ hipError_t launch_k(const LaunchArgs& a, int kind, const SeqTable* seqs, const G
     const dim3 grid((unsigned)(a.chains * tiles));
     if constexpr (K <= 128) {
         if (kind == 2) {
-            hipLaunchKernelGGL((correct_h0_grouped_kernel<K, false>), grid, dim3(64 * Grouped<K>::WAVES), 0,
-                               (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles, a.heads, K, *table);
+            hipLaunchKernelGGL((correct_h0_grouped_kernel<K>), grid, dim3(grouped_threads<K>()), 0,
+                               (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles, a.heads, *table);
             return hipGetLastError();
         }
         return kind == 1 ? launch_dma_varlen<K, LAYOUT, DIR>(a, grid, tiles, *seqs)
@@ -1338,9 +1386,8 @@ hipError_t launch_k(const LaunchArgs& a, int kind, const SeqTable* seqs, const G
         constexpr bool PAD = K != 256;
         const int threads = 64 * general_waves(DIR == QLA_DIR_FWD);
         if (kind == 2) {
-            hipLaunchKernelGGL((correct_h0_grouped_kernel<256, PAD>), grid, dim3(64 * Grouped<256, PAD>::WAVES), 0,
-                               (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles, a.heads, a.K,
-                               *table);
+            hipError_t e = launch_grouped_dir<QLA_DIR_FWD, PAD>(a, tiles, *table);
+            return e != hipSuccess ? e : launch_grouped_dir<QLA_DIR_BWD, PAD>(a, tiles, *table);
         } else if (kind == 1) {
             hipLaunchKernelGGL((correct_h0_varlen_kernel<LAYOUT, DIR, PAD>), grid, dim3(threads), 0,
                                (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.heads, a.V, tiles, a.K, *seqs);
@@ -1387,7 +1434,7 @@ hipError_t dispatch(const LaunchArgs& a, int layout, int direction, int kind, co
 
 int tiles_for(int V) { return (V + kTileV - 1) / kTileV; }
 
-int max_threads_per_group() { return dma_threads<128>() > 64 * kGroupedWaves ? dma_threads<128>() : 64 * kGroupedWaves; }
+int max_threads_per_group() { return dma_threads<128>() > 64 * general_waves(true) ? dma_threads<128>() : 64 * general_waves(true); }
 
 hipError_t launch_correct_h0(const LaunchArgs& a)
 {

@@ -66,10 +66,11 @@ def test_grouped_in_place():
     assert torch.equal(Hd.view(torch.int32), sep.view(torch.int32))
 
 
-@pytest.mark.parametrize("K", [32, 64, 112, 128])
+@pytest.mark.parametrize("K", [32, 64, 112, 128, 160, 256])
 def test_grouped_matches_plain_calls_bitwise(K):
-    """At K <= 128 a grouped call runs the same per-chain code as plain calls:
-    every group's output equals, bit for bit, a plain call on that group's heads."""
+    """A grouped call runs the same per-chain code as plain calls (at K > 128 as
+    one launch per direction, with the plain kernels' block shapes): every
+    group's output equals, bit for bit, a plain call on that group's heads."""
     import torch
 
     import linear_attention_context_amd as qla

@@ -33,7 +33,7 @@ VMEM = re.compile(r"^(buffer_|global_)")
 # kernels with producer waves: the plain and variable-length K <= 128 kernels of
 # both directions, and the grouped kernel at K <= 128 (mangled names)
 K_DMA = (16, 32, 48, 64, 80, 96, 112, 128)
-PRODUCER_KERNELS = re.compile(r"correct_h0_(fwd|bwd)_dma|correct_h0_grouped_kernelILi(%s)ELb0E" % "|".join(map(str, K_DMA)))
+PRODUCER_KERNELS = re.compile(r"correct_h0_(fwd|bwd)_dma|correct_h0_grouped_kernelILi(%s)E" % "|".join(map(str, K_DMA)))
 
 
 def _tools():
