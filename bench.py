@@ -48,7 +48,7 @@ METRIC = "segment-state corrections/s + achieved HBM GB/s (% roofline), 32K tok 
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_context_amd", "csrc", "qla_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "correct_h0_fwd_32k32h_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "correct_h0_32k32h_traffic.md")
 # The correction note (Antarx Memos), performance section, table of the 32K x
 # 32-head correction kernel: per-call latency of the final (membar) scheme on
 # an H100, timed as a graph of 16 calls.  Another machine and unstated head
@@ -166,12 +166,18 @@ def run_sweep(args) -> int:
                 sets = [dict(H=torch.from_numpy(Hl).to(dev), M=torch.from_numpy(M).to(dev),
                              S0=torch.from_numpy(Sl).to(dev), out=torch.empty(Hl.shape, device=dev))
                         for _ in range(rot)]
-                # untimed: calls on freshly allocated buffers run slow until about a
-                # thousand calls have gone over them
-                for i in range(1024):
+                # untimed calls first, at least --warmup-seconds of them: an idle GPU
+                # runs at a low clock and needs tens of ms of continuous work to
+                # reach its working clock
+                t_w, i = time.perf_counter(), 0
+                while i < 64 or time.perf_counter() - t_w < args.warmup_seconds:
                     x = sets[i % rot]
                     qla.qla_correct_h0(x["H"], x["M"], x["S0"], x["out"], layout, "fwd", 1, heads, n, K, V,
                                        stream=stream.cuda_stream)
+                    i += 1
+                    if i % 64 == 0:
+                        torch.cuda.synchronize()
+                torch.cuda.synchronize()
                 for direction in ("fwd", "bwd"):
                     for s0_on in (True, False):
                         def call(x):
@@ -248,13 +254,18 @@ def run_configs(args) -> int:
                     qla.qla_correct_h0(x["H"], x["M"], x["S0"], x["out"], what[0], what[1], B, NH, N, K, V,
                                        stream=stream.cuda_stream)
             reps = 64 if nbytes < (64 << 20) else 8
-            # untimed calls first: calls on freshly allocated buffers run slow
-            # until about a thousand calls have gone over them
-            n_warm = 1024 if nbytes < (64 << 20) else 8
             times = {}
             for kind, order in (("warm", [0] * reps), ("rotated", [i % rot for i in range(max(reps, rot))])):
-                for i in range(n_warm):
+                # untimed calls first, at least --warmup-seconds of them: an idle
+                # GPU runs at a low clock and needs tens of ms of continuous
+                # work to reach its working clock
+                t_w, i = time.perf_counter(), 0
+                while i < 8 or time.perf_counter() - t_w < args.warmup_seconds:
                     call(sets[order[i % len(order)]])
+                    i += 1
+                    if i % 16 == 0:
+                        torch.cuda.synchronize()
+                torch.cuda.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 for i in order:
