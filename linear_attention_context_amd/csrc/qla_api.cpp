@@ -3,6 +3,7 @@
 // contract are documented in include/qla.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "qla.h"
@@ -85,6 +86,27 @@ int check_buffers(const float* H, const float* M, const float* S0, const float* 
     return QLA_OK;
 }
 
+// Compute units of the current device, queried once per device (an
+// immutable property: a racing first query stores the same value).
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -99,7 +121,7 @@ int qla_correct_h0(const float* H, const float* M, const float* S0, float* out, 
     if (chains == 0 || n_seg == 0) return QLA_OK;
     if ((rc = check_buffers(H, M, S0, out, chains, chains * n_seg, K, V)) != QLA_OK) return rc;
 
-    qla::LaunchArgs a{H, M, S0, out, layout, direction, chains, heads, n_seg, K, V, stream};
+    qla::LaunchArgs a{H, M, S0, out, layout, direction, chains, heads, n_seg, K, V, stream, device_cus()};
     return qla::launch_correct_h0(a) == hipSuccess ? QLA_OK : QLA_ERR_LAUNCH;
 }
 
@@ -138,7 +160,7 @@ int qla_correct_h0_grouped(const float* H, const float* M, const float* S0, floa
     if (chains == 0 || n_seg == 0) return QLA_OK;
     if ((rc = check_buffers(H, M, S0, out, chains, chains * n_seg, K, V)) != QLA_OK) return rc;
 
-    qla::LaunchArgs a{H, M, S0, out, -1, -1, chains, heads, n_seg, K, V, stream};
+    qla::LaunchArgs a{H, M, S0, out, -1, -1, chains, heads, n_seg, K, V, stream, device_cus()};
     return qla::launch_correct_h0_grouped(a, table) == hipSuccess ? QLA_OK : QLA_ERR_LAUNCH;
 }
 
@@ -163,7 +185,7 @@ int qla_correct_h0_varlen(const float* H, const float* M, const float* S0, float
     if (chains == 0 || segments == 0) return QLA_OK;
     if ((rc = check_buffers(H, M, S0, out, chains, segments, K, V)) != QLA_OK) return rc;
 
-    qla::LaunchArgs a{H, M, S0, out, layout, direction, chains, heads, -1, K, V, stream};
+    qla::LaunchArgs a{H, M, S0, out, layout, direction, chains, heads, -1, K, V, stream, device_cus()};
     return qla::launch_correct_h0_varlen(a, seqs) == hipSuccess ? QLA_OK : QLA_ERR_LAUNCH;
 }
 

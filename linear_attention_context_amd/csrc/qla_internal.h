@@ -23,6 +23,7 @@ struct LaunchArgs {
     int K;
     int V;
     void* stream;
+    int cus;  // compute units of the device (a K <= 128 workgroup occupies one CU)
 };
 
 // Head-group table copied by value into the grouped kernel's arguments.

@@ -231,11 +231,13 @@ struct Tile {
     static constexpr int vec_of(int t, int r) { return (KV || FWD) ? t : (T * r + t) >> 2; }
     static constexpr int comp_of(int t, int r) { return (KV || FWD) ? r : (T * r + t) & 3; }
 
-    static __device__ __forceinline__ Lane make_lane(int v0, int V, int kp = K)
+    // wave: the wave's index among the MFMA waves that share this tile
+    // (default: its index in the workgroup).
+    static __device__ __forceinline__ Lane make_lane(int v0, int V, int kp = K, int wave = -1)
     {
         Lane L;
         const int lane = threadIdx.x & 63;
-        L.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        L.wave = wave >= 0 ? wave : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         L.g = lane >> 4;
         L.c = lane & 15;
         L.a0 = L.wave * S::ROWS;
@@ -791,12 +793,14 @@ struct Tile {
 // of either direction are free of bank conflicts (backward, the four rows a
 // read instruction touches differ in bits 2-3 of k, which moves their chunks
 // to distinct banks).
-template <int K, int LAYOUT, int DIR = QLA_DIR_FWD>
+template <int K, int LAYOUT, int DIR = QLA_DIR_FWD, int G = 1>
 struct DmaChain {
     static_assert(K % 16 == 0 && K >= 16 && K <= 128, "producer kernels cover K = 16 .. 128");
-    static constexpr int CW = K / 16;                  // MFMA waves, 16 rows each
+    static_assert(G == 1 || (G == 2 && K % 32 == 0), "two groups of waves with 32 rows each");
+    static constexpr int CW = K / 16;                  // MFMA waves
+    static constexpr int CWG = CW / G;                 // MFMA waves per group, 16 G rows each
     static constexpr int PW = kProducers;              // producer waves
-    using Tl = Tile<K, LAYOUT, QLA_DIR_FWD, CW>;
+    using Tl = Tile<K, LAYOUT, QLA_DIR_FWD, CWG>;
     using S = typename Tl::S;
     using Lane = typename Tl::Lane;
     using Chain = typename Tl::Chain;
@@ -805,19 +809,20 @@ struct DmaChain {
     // Staged operand of (t, block b): forward M[a0 + 16t + c][k] (the wave's
     // rows, one 16-byte read); backward M[k][a0 + 16t + c] (a column, four
     // 4-byte reads), k = 16 kb + 4g + q.
-    static __device__ __forceinline__ f4 rd(const float* st, int t, int b, const Lane& L, const int (&X_tofs)[4])
+    template <int NT>
+    static __device__ __forceinline__ f4 rd(const float* st, int t, int b, const Lane& L, const int (&X_tofs)[NT][4])
     {
         if constexpr (DIR == QLA_DIR_FWD) {
             return Tl::stage_read(st, t, b, L);
         } else {
             // k & 15 = 4g + q does not depend on the block, so the lane's four
-            // byte offsets (tofs) are fixed; the block adds a uniform 16 K-float step.
-            static_assert(T == 1, "one row tile per wave");
+            // byte offsets per row tile (tofs) are fixed; the block adds a
+            // uniform 16 K-float step.
             const int kofs = __builtin_amdgcn_readfirstlane((int)Tl::wrapb(b + L.brot) * 16 * K * 4);
             const char* sb = reinterpret_cast<const char*>(st) + kofs;
             f4 v;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const float*>(sb + X_tofs[q]);
+            for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const float*>(sb + X_tofs[t][q]);
             return v;
         }
     }
@@ -846,7 +851,7 @@ struct DmaChain {
         const float* cur;
         const float* st;
         __amdgpu_buffer_rsrc_t out_prev;
-        int tofs[4];  // backward: byte offsets of the lane's staged column reads
+        int tofs[T][4];  // backward: byte offsets of the lane's staged column reads, per row tile
     };
 
     // L2 warm-up loads, issued by the producers right after each step's copy.
@@ -948,6 +953,84 @@ struct DmaChain {
             warm_m(C, sink, s + 1 + kMTouch, p, tile, tiles);
             warm_h(C, sink, s + 1 + HA, p, tile, V);
             asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWarmPerStep) : "memory");
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+
+    // Two groups (G = 2): workgroup tp carries tiles tp and tp + pairs of one
+    // chain, one per group of MFMA waves, and a barrier falls every half
+    // step.  (In the kv layout a 128-byte line of a row holds the 64-byte
+    // pieces of tiles 2m and 2m + 1: they belong to the same group of two
+    // neighbouring workgroups, which run in phase on one XCD, so L2 merges
+    // the halves of each out line as it does for single tiles.  Tiles 2 tp and
+    // 2 tp + 1 in one workgroup would write them half a step apart, and a
+    // third more bytes reached memory.)  Group 0 runs step s from barrier 2s to barrier 2s+2, group 1 from
+    // 2s+1 to 2s+3.  Both read M_s from stage s&1, so M_j (j >= 2) may
+    // overwrite M_{j-2} only after barrier 2j-1, where group 1 finishes step
+    // j-2, and must have landed by barrier 2j, where group 0 starts step j:
+    // the producers copy it between those two barriers.  M_0 is copied
+    // before barrier 0 and M_1 (stage 1, unused until then) between barriers
+    // 0 and 1.  The warm-ups ride behind each copy as above: the lines of
+    // M_{j+kPairTouch} and the two tiles' H lines of step j+HA.  A step here
+    // takes about twice as long as a single tile's, and twice as many chains
+    // share an XCD's L2, so M is warmed one step ahead (two measured 1.2-1.5x
+    // the algorithmic reads: lines fell out of L2 before their copy).
+    static constexpr int kPairTouch = 1;
+    // Slot i = p + PW*lane: i < 128 tile A, 128 .. 255 tile B.  kv: one word in
+    // each row's 64-byte piece of the tile, every other row when the partner
+    // tile exists (its workgroup warms the rest of the 128-byte lines); vk:
+    // one word in each of the tile's K/2 lines.
+    static __device__ __forceinline__ void warm_h_pair(const Chain& C, float* sink, int s, int p, int tA, int tB,
+                                                       int V)
+    {
+        const bool live = s < C.n_seg;
+        const unsigned bytes = (unsigned)K * V * 4u;
+        const __amdgpu_buffer_rsrc_t r = rsrc(C.H + (size_t)sg(C, live ? s : 0) * (bytes / 4), live ? bytes : 0u);
+        const int i = p + PW * (int)(threadIdx.x & 63);
+        const int t = i < 128 ? tA : tB;
+        const int j = i & 127;
+        unsigned off = kOutOfRange;
+        if constexpr (LAYOUT == QLA_LAYOUT_KV) {
+            const int tiles = (V + kTileV - 1) / kTileV;
+            const bool partner = (t ^ 1) < tiles;
+            const int row = partner ? 2 * j + (t & 1) : j;
+            if (row < K && (partner ? j < K / 2 : true)) off = 4u * (unsigned)(row * V) + 64u * (unsigned)t;
+        } else {
+            if (j < K / 2) off = 64u * (unsigned)K * (unsigned)t + 128u * (unsigned)j;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)sink, 4, (int)off, 0, 0, 0);
+    }
+
+    static __device__ __forceinline__ void copy_unit(const Chain& C, float* lds, int j, int p, int tp, int pairs,
+                                                     int V)
+    {
+        float* sink = lds + WARM;
+        dma_unit(C.M + (size_t)sg(C, j) * K * K, lds + S::STATE_FLOATS + (j & 1) * STAGE, sink, p);
+        copies_before_warmups();
+        warm_m(C, sink, j + kPairTouch, p, tp, pairs);
+        warm_h_pair(C, sink, j + HA, p, tp, tp + pairs, V);
+    }
+
+    static __device__ __forceinline__ void producer_pair(const Chain& C, float* lds, int p, int tp, int V)
+    {
+        float* sink = lds + WARM;
+        const int pairs = ((V + kTileV - 1) / kTileV + 1) / 2;
+        dma_unit(C.M + (size_t)sg(C, 0) * K * K, lds + S::STATE_FLOATS, sink, p);
+        copies_before_warmups();
+#pragma unroll
+        for (int u = 1; u <= kPairTouch; ++u) warm_m(C, sink, u, p, tp, pairs);
+        warm_h_pair(C, sink, HA, p, tp, tp + pairs, V);
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kPairTouch + 1) : "memory");
+        // after barrier k, before barrier k + 1 (k = 0 .. 2n-1)
+        for (int k = 0; k < 2 * C.n_seg; ++k) {
+            const int j = k == 0 ? 1 : ((k & 1) && k >= 3 ? (k + 1) / 2 : -1);
+            if (j >= 1 && j < C.n_seg) {
+                debug_delay(p, j, 2);  // a late copy: both groups must wait for it at the barrier
+                copy_unit(C, lds, j, p, tp, pairs, V);
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWarmPerStep) : "memory");
+            } else {
+                asm volatile("s_barrier" ::: "memory");
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -1063,21 +1146,29 @@ struct DmaChain {
         }
     }
 
+    // Backward: the lane's byte offsets of its staged column reads, row tile
+    // t, instruction q (row k = 4g + q of a 16-k block, column a0 + 16t + c).
+    static __device__ __forceinline__ void init_tofs(Ctx& X, const Lane& L)
+    {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (DIR != QLA_DIR_FWD) {
+                    const int col = L.a0 + 16 * t + L.c;
+                    const int r = 4 * L.g + q;
+                    X.tofs[t][q] = 4 * (r * K + 4 * ((col >> 2) ^ (r & (SWZ - 1))) + (col & 3));
+                } else {
+                    X.tofs[t][q] = 0;
+                }
+            }
+    }
+
     static __device__ __forceinline__ void consumer(const Chain& C, const float* S0c, float* lds, int tile, int V)
     {
         const Lane L = Tl::make_lane(tile * kTileV, V);
         Ctx X;
-        if constexpr (DIR != QLA_DIR_FWD) {
-            const int col = L.a0 + L.c;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int r = 4 * L.g + q;
-                X.tofs[q] = 4 * (r * K + 4 * ((col >> 2) ^ (r & (SWZ - 1))) + (col & 3));
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) X.tofs[q] = 0;
-        }
+        init_tofs(X, L);
         f4 h[HR][T];
         f4 sv[T];
         Tl::load_state(sv, rsrc(S0c ? S0c : C.H, S0c ? L.state_bytes : 0u), L);
@@ -1102,6 +1193,110 @@ struct DmaChain {
                         L);
     }
 
+    // One step of a group (G = 2), entered right after the barrier that opens
+    // it: the stage and state reads, the first half of the MFMA blocks, the
+    // mid-step barrier (the other group's step boundary; every read of this
+    // group's state slot has returned before it, so the slot can then take
+    // the new state), the second half with out of step s-1 and H of step
+    // s+HA, the new state into the slot, and the barrier that closes the step
+    // unless this is group 1's last step (group 1 ends one barrier after the
+    // others' last).
+    static constexpr int kMid = BP / 2;
+    static constexpr int kS2 = kStoreAt > kMid ? kStoreAt : kMid;
+    static constexpr int kL2 = kLoadAt > kS2 ? kLoadAt : kS2;
+    template <int LSX>
+    static __device__ __forceinline__ void step_pair(int s, int g, Ctx& X, const Chain& C, f4 (&h)[HR][T], float* lds,
+                                                     float* slot, const Lane& L)
+    {
+        s = __builtin_amdgcn_readfirstlane(s);
+        const int jp = s > 0 ? sg(C, s - 1) : 0;
+        X.out_prev = rsrc(C.out + (size_t)jp * (L.state_bytes / 4), s > 0 ? L.state_bytes : 0u);
+        const bool live = s + HA < C.n_seg;
+        const __amdgpu_buffer_rsrc_t Hr =
+            rsrc(C.H + (size_t)(live ? sg(C, s + HA) : 0) * (L.state_bytes / 4), live ? L.state_bytes : 0u);
+
+        __builtin_amdgcn_sched_barrier(0);
+        debug_delay(L.wave, s, 0);
+        X.cur = slot;
+        X.st = lds + S::STATE_FLOATS + (s & 1) * STAGE + (DIR == QLA_DIR_FWD ? L.a0 * K : 0);
+#pragma unroll
+        for (int b = 0; b < kFirstReads; ++b)
+#pragma unroll
+            for (int t = 0; t < T; ++t) X.mo[b][t] = rd(X.st, t, b, L, X.tofs);
+        Tl::template read_pv<0, kOwn, BP>(X.pv, X.cur, L);
+        {
+            f4 hx[T];
+            Tl::frag_from_vecs(hx, h[LSX]);
+#pragma unroll
+            for (int t = 0; t < T; ++t) X.acc[t] = hx[t];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        blocks<0, kMid>(X, L);
+        lds_handoff();
+        blocks<kMid, kS2>(X, L);
+        Tl::store_state(X.out_prev, X.own, L);
+        __builtin_amdgcn_sched_barrier(0);
+        blocks<kS2, kL2>(X, L);
+        Tl::load_state(h[(LSX + HA) % HR], Hr, L);
+        __builtin_amdgcn_sched_barrier(0);
+        blocks<kL2, BP>(X, L);
+
+        debug_delay(L.wave, s, 1);
+        Tl::put_state(slot, X.acc, L);
+#pragma unroll
+        for (int t = 0; t < T; ++t) X.own[t] = X.acc[t];
+        __builtin_amdgcn_sched_barrier(0);
+        if (!(g == 1 && s + 1 == C.n_seg)) lds_handoff();
+    }
+
+    template <int LSX>
+    static __device__ __forceinline__ void tail_pair(int s, int g, Ctx& X, const Chain& C, f4 (&h)[HR][T],
+                                                     float* lds, float* slot, const Lane& L)
+    {
+        if constexpr (LSX < HR - 1) {
+            if (s + LSX < C.n_seg) {
+                step_pair<LSX>(s + LSX, g, X, C, h, lds, slot, L);
+                tail_pair<LSX + 1>(s, g, X, C, h, lds, slot, L);
+            }
+        }
+    }
+
+    static __device__ __forceinline__ void consumer_pair(const Chain& C, const float* S0c, float* lds, int tp,
+                                                         int V)
+    {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int g = wave / CWG;
+        const int pairs = ((V + kTileV - 1) / kTileV + 1) / 2;
+        const Lane L = Tl::make_lane((tp + g * pairs) * kTileV, V, K, wave - g * CWG);
+        float* slot = lds + g * (kTileV * LS);  // the group's one state slot
+        Ctx X;
+        init_tofs(X, L);
+        f4 h[HR][T];
+        f4 sv[T];
+        Tl::load_state(sv, rsrc(S0c ? S0c : C.H, S0c ? L.state_bytes : 0u), L);
+#pragma unroll
+        for (int i = 0; i < HA; ++i) {
+            const bool live = i < C.n_seg;
+            Tl::load_state(h[i], rsrc(C.H + (size_t)sg(C, live ? i : 0) * (L.state_bytes / 4),
+                                      live ? L.state_bytes : 0u), L);
+        }
+        Tl::frag_from_vecs(X.own, sv);
+        Tl::put_state(slot, X.own, L);
+        lds_handoff();             // barrier 0: both initial states and M_0 in place
+        if (g == 1) lds_handoff(); // barrier 1: group 1 starts half a step later
+        int s = 0;
+        for (; s + HR <= C.n_seg; s += HR) {
+            step_pair<0>(s, g, X, C, h, lds, slot, L);
+            if constexpr (HR > 1) step_pair<1 % HR>(s + 1, g, X, C, h, lds, slot, L);
+            if constexpr (HR > 2) step_pair<2 % HR>(s + 2, g, X, C, h, lds, slot, L);
+            if constexpr (HR > 3) step_pair<3 % HR>(s + 3, g, X, C, h, lds, slot, L);
+            if constexpr (HR > 4) step_pair<4 % HR>(s + 4, g, X, C, h, lds, slot, L);
+        }
+        tail_pair<0>(s, g, X, C, h, lds, slot, L);
+        Tl::store_state(rsrc(C.out + (size_t)sg(C, C.n_seg - 1) * (L.state_bytes / 4), L.state_bytes), X.own,
+                        L);
+    }
+
     static __device__ __forceinline__ void run(const float* H, const float* M, const float* S0, float* out,
                                                int n_seg, int V, size_t chain, int tile, float* lds)
     {
@@ -1116,8 +1311,14 @@ struct DmaChain {
         // A chain without segments: every wave leaves before any barrier.
         if (__builtin_amdgcn_readfirstlane(C.n_seg) <= 0) return;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        if (wave >= CW) producer(C, lds, wave - CW, tile, V);
-        else consumer(C, S0c, lds, tile, V);
+        if constexpr (G == 1) {
+            if (wave >= CW) producer(C, lds, wave - CW, tile, V);
+            else consumer(C, S0c, lds, tile, V);
+        } else {
+            // tile: the pair index
+            if (wave >= CW) producer_pair(C, lds, wave - CW, tile, V);
+            else consumer_pair(C, S0c, lds, tile, V);
+        }
     }
 };
 
@@ -1166,6 +1367,20 @@ __global__ __launch_bounds__(dma_threads<K>()) void correct_h0_fwd_dma_kernel(
     const int chain = id / tiles;
     const int tile = id - chain * tiles;
     D::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds);
+}
+
+// Two 16-column tiles of a chain per workgroup (tiles tp and tp + pairs), half
+// a step apart (K a multiple of 32): grids of at least two tiles per CU.
+template <int K, int LAYOUT, int DIR>
+__global__ __launch_bounds__(dma_threads<K>()) void correct_h0_pair_kernel(
+    const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int pairs)
+{
+    using D = DmaChain<K, LAYOUT, DIR, 2>;
+    __shared__ __attribute__((aligned(16))) float lds[D::LDS_FLOATS];
+    const int id = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int chain = id / pairs;
+    const int tp = id - chain * pairs;
+    D::run(H, M, S0, out, n_seg, V, (size_t)chain, tp, lds);
 }
 
 template <int K, int LAYOUT>
@@ -1378,6 +1593,18 @@ hipError_t launch_k(const LaunchArgs& a, int kind, const SeqTable* seqs, const G
             hipLaunchKernelGGL((correct_h0_grouped_kernel<K>), grid, dim3(grouped_threads<K>()), 0,
                                (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles, a.heads, *table);
             return hipGetLastError();
+        }
+        if constexpr (K % 32 == 0) {
+            // At least two 16-column tiles per CU: pairs of tiles, half a step
+            // apart, so that one tile's step boundary overlaps the other's
+            // matrix work.
+            if (kind == 0 && tiles >= 2 && (long long)a.chains * tiles >= 2LL * a.cus) {
+                const int pairs = (tiles + 1) / 2;
+                hipLaunchKernelGGL((correct_h0_pair_kernel<K, LAYOUT, DIR>), dim3((unsigned)(a.chains * pairs)),
+                                   dim3(dma_threads<K>()), 0, (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg,
+                                   a.V, pairs);
+                return hipGetLastError();
+            }
         }
         return kind == 1 ? launch_dma_varlen<K, LAYOUT, DIR>(a, grid, tiles, *seqs)
                          : launch_dma<K, LAYOUT, DIR>(a, grid, tiles);

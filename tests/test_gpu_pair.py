@@ -1,0 +1,101 @@
+"""GPU tests of the two-tile producer kernel.
+
+Plain calls at K a multiple of 32 (up to 128) whose grid has at least two
+16-column tiles per compute unit run two tiles of a chain per workgroup, in
+two groups of MFMA waves half a step apart.  These shapes are sized past that
+threshold.  Every variant is compared with the fp64 oracle: with and without
+S0, and with a ragged V whose last pair has one tile only.  Exact inputs and
+coded sentinels must come back bit for bit, chains of 1-3 segments exercise
+the barrier schedule's ends, and the forced-delay build and repeated calls
+must give identical bits.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import qla_inputs as qi
+from gpu_util import assert_parity, bits, decode_mismatch, lay, oracle_threaded, run_hip, to_device
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = [("kv", "fwd"), ("kv", "bwd"), ("vk", "fwd"), ("vk", "bwd")]
+
+
+def _cus():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def _pair_shape(V):
+    """(batch, heads) with at least two 16-column tiles per compute unit."""
+    tiles = (V + 15) // 16
+    chains = -(-2 * _cus() // tiles)
+    heads = -(-chains // 2)
+    return 2, heads
+
+
+@pytest.mark.parametrize("K", [32, 64, 96, 128])
+@pytest.mark.parametrize("layout,direction", VARIANTS)
+def test_pair_parity(K, layout, direction):
+    V = 100 if K >= 64 else 52  # ragged: 7 or 4 tiles (the last pair of 7 has one tile)
+    B, NH = _pair_shape(V)
+    for with_s0 in (True, False):
+        H, M, S0 = qi.random_case(3000 + K, (B, NH), 5, K, V, with_s0=with_s0)
+        print(f"  pair K={K} V={V} {B}x{NH} {layout} {direction} s0={with_s0}", flush=True)
+        got = run_hip(lay(H, layout), M, lay(S0, layout), layout, direction).cpu().numpy()
+        ref = oracle_threaded(lay(H, layout), M, lay(S0, layout), layout, direction)
+        assert_parity(got, ref, f"pair K={K} V={V} {B}x{NH} {layout} {direction} s0={with_s0}")
+
+
+@pytest.mark.parametrize("K", [64, 128])
+@pytest.mark.parametrize("layout,direction", VARIANTS)
+def test_pair_exact_inputs_and_sentinels(K, layout, direction):
+    """Signed permutations with small integers (every fp32 operation exact)
+    and the M = 0 coded sentinel: bit for bit."""
+    V, n = 128, 4
+    B, NH = _pair_shape(V)
+    H = qi.small_integers(3100 + K, (B, NH, n, K, V))
+    S0 = qi.small_integers(3102 + K, (B, NH, K, V))
+    M = qi.signed_permutations(3101 + K, (B, NH, n), K)
+    ref = oracle.correct_h0(lay(H, layout), M, lay(S0, layout), layout, direction)
+    want = ref.astype(np.float32)
+    assert np.array_equal(ref, want.astype(np.float64))
+    got = run_hip(lay(H, layout), M, lay(S0, layout), layout, direction).cpu().numpy()
+    assert np.array_equal(bits(got), bits(want)), decode_mismatch(got, want)
+    coded = qi.coded_states((B, NH), n, K, V)
+    got = run_hip(lay(coded, layout), np.zeros_like(M), lay(S0, layout), layout, direction).cpu().numpy()
+    assert np.array_equal(bits(got), bits(lay(coded, layout))), decode_mismatch(got, lay(coded, layout))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3])
+@pytest.mark.parametrize("layout,direction", VARIANTS)
+def test_pair_short_chains(n, layout, direction):
+    K = V = 128
+    B, NH = _pair_shape(V)
+    H, M, S0 = qi.random_case(3200 + n, (B, NH), n, K, V)
+    got = run_hip(lay(H, layout), M, lay(S0, layout), layout, direction).cpu().numpy()
+    ref = oracle_threaded(lay(H, layout), M, lay(S0, layout), layout, direction)
+    assert_parity(got, ref, f"pair n={n} {layout} {direction}")
+
+
+@pytest.mark.parametrize("layout,direction", VARIANTS)
+def test_pair_forced_delay_and_repeat_identical(layout, direction):
+    """The forced-delay build gives the same bits; so do 20 repeated calls
+    with out cleared to NaN before each."""
+    import torch
+
+    import linear_attention_context_amd as qla
+    delay = qla.load_library(qla.library_path("delay"))
+    K, V, n = 128, 96, 6
+    B, NH = _pair_shape(V)
+    H, M, S0 = qi.random_case(3300, (B, NH), n, K, V)
+    a = run_hip(lay(H, layout), M, lay(S0, layout), layout, direction)
+    b = run_hip(lay(H, layout), M, lay(S0, layout), layout, direction, lib=delay)
+    assert np.array_equal(bits(a), bits(b))
+    Hd, Md, Sd = to_device(lay(H, layout)), to_device(M), to_device(lay(S0, layout))
+    out = torch.empty_like(Hd)
+    for _ in range(20):
+        out.fill_(float("nan"))
+        qla.qla_correct_h0(Hd, Md, Sd, out, layout, direction, B, NH, n, K, V)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32).cpu(), a.view(torch.int32).cpu())
