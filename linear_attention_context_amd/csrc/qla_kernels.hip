@@ -822,7 +822,7 @@ struct DmaChain {
             const char* sb = reinterpret_cast<const char*>(st) + kofs;
             f4 v;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const float*>(sb + X_tofs[t][q]);
+            for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const float*>(sb + X_tofs[t][0] + q * K * 4);
             return v;
         }
     }
@@ -837,6 +837,17 @@ struct DmaChain {
     // copy counts differ and the spare copies (1 KiB, of nothing) land there.
     static constexpr int LDS_FLOATS = WARM + (kDmaAll % kProducers ? 256 : 64);
     static constexpr int SWZ = S::SWZ;                // chunk swizzle of a stage row
+    // The XOR applied to a stage row's chunk index.  Forward: the row's low
+    // bits (16 rows of one 16-byte read each spread over all banks).
+    // Backward: the row's bits 2 and up, the low two cleared, so the four
+    // rows 4g .. 4g+3 that one lane reads per 16-k block share it: their
+    // words lie exactly one row apart and the compiler pairs them into
+    // two-address LDS reads (half the read instructions).  A 64-lane read then
+    // hits every bank twice, the minimum for 256 bytes.
+    static __device__ __forceinline__ int swz_row(int row)
+    {
+        return DIR == QLA_DIR_FWD ? (row & (SWZ - 1)) : ((row & ~3) & (SWZ - 1));
+    }
     static constexpr int kDma = kDmaAll;
     static constexpr int kPer = (kDma + PW - 1) / PW; // copies per producer (the last ones may be empty)
     static constexpr int HA = kHAhead;                // H is loaded HA steps ahead
@@ -916,7 +927,7 @@ struct DmaChain {
             const bool real = kDma % PW == 0 || i < kDma;
             const int q = 256 * i + 4 * lane;
             const int row = q / K, chunk = (q % K) / 4;
-            const int src = row * K + 4 * (chunk ^ (row & (SWZ - 1)));
+            const int src = row * K + 4 * (chunk ^ swz_row(row));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(real ? stage + 256 * i : sink),
                                                      16, real ? 4 * src : (int)kOutOfRange, 0, 0, 0);
         }
@@ -1157,7 +1168,7 @@ struct DmaChain {
                 if constexpr (DIR != QLA_DIR_FWD) {
                     const int col = L.a0 + 16 * t + L.c;
                     const int r = 4 * L.g + q;
-                    X.tofs[t][q] = 4 * (r * K + 4 * ((col >> 2) ^ (r & (SWZ - 1))) + (col & 3));
+                    X.tofs[t][q] = 4 * (r * K + 4 * ((col >> 2) ^ swz_row(r)) + (col & 3));
                 } else {
                     X.tofs[t][q] = 0;
                 }
@@ -1233,6 +1244,12 @@ struct DmaChain {
         __builtin_amdgcn_sched_barrier(0);
         blocks<0, kMid>(X, L);
         lds_handoff();
+        // The second half: this group's step ends at the next barrier.  Its
+        // waves take issue priority over the other group's (in the first half
+        // of its step), so its MFMAs finish first and the other group's
+        // remaining MFMAs keep the matrix cores busy while this group writes
+        // its state and reaches the barrier.
+        __builtin_amdgcn_s_setprio(1);
         blocks<kMid, kS2>(X, L);
         Tl::store_state(X.out_prev, X.own, L);
         __builtin_amdgcn_sched_barrier(0);
@@ -1247,6 +1264,7 @@ struct DmaChain {
         for (int t = 0; t < T; ++t) X.own[t] = X.acc[t];
         __builtin_amdgcn_sched_barrier(0);
         if (!(g == 1 && s + 1 == C.n_seg)) lds_handoff();
+        __builtin_amdgcn_s_setprio(0);
     }
 
     template <int LSX>
