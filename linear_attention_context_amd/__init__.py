@@ -79,6 +79,7 @@ def qla_status_str(status: int, lib: ctypes.CDLL | None = None) -> str:
     return (lib or load_library()).qla_status_str(int(status)).decode()
 
 
+QLA_ERR_LAUNCH = -7
 QLA_ERR_MEMORY = -8
 _BAD = object()   # a tensor argument the library must not see
 _F32 = None

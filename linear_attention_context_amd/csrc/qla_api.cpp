@@ -107,9 +107,38 @@ int device_cus()
     return n;
 }
 
+// The launchers report failure through the thread's last runtime error
+// (hipGetLastError after the launch): clear whatever an earlier, unrelated
+// call left there first, so that it is not taken for a failed launch.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+#if defined(QLA_DEBUG_DELAY) && QLA_DEBUG_DELAY
+// Test build only (the forced-delay library): qla_test_fail_launches(n) makes
+// the next n launches report a runtime rejection, so that the QLA_ERR_LAUNCH
+// path of every entry point can be exercised without a failing launch.
+std::atomic<int> g_fail_launches{0};
+bool injected_failure()
+{
+    int n = g_fail_launches.load();
+    while (n > 0 && !g_fail_launches.compare_exchange_weak(n, n - 1)) {
+    }
+    return n > 0;
+}
+#else
+constexpr bool injected_failure() { return false; }
+#endif
+
 }  // namespace
 
 extern "C" {
+
+#if defined(QLA_DEBUG_DELAY) && QLA_DEBUG_DELAY
+QLA_API int qla_test_fail_launches(int n)
+{
+    g_fail_launches.store(n > 0 ? n : 0);
+    return QLA_OK;
+}
+#endif
 
 int qla_correct_h0(const float* H, const float* M, const float* S0, float* out, int layout, int direction,
                    int batch, int heads, int n_seg, int K, int V, void* stream)
@@ -122,6 +151,8 @@ int qla_correct_h0(const float* H, const float* M, const float* S0, float* out, 
     if ((rc = check_buffers(H, M, S0, out, chains, chains * n_seg, K, V)) != QLA_OK) return rc;
 
     qla::LaunchArgs a{H, M, S0, out, layout, direction, chains, heads, n_seg, K, V, stream, device_cus()};
+    if (injected_failure()) return QLA_ERR_LAUNCH;
+    clear_stale_error();
     return qla::launch_correct_h0(a) == hipSuccess ? QLA_OK : QLA_ERR_LAUNCH;
 }
 
@@ -161,6 +192,8 @@ int qla_correct_h0_grouped(const float* H, const float* M, const float* S0, floa
     if ((rc = check_buffers(H, M, S0, out, chains, chains * n_seg, K, V)) != QLA_OK) return rc;
 
     qla::LaunchArgs a{H, M, S0, out, -1, -1, chains, heads, n_seg, K, V, stream, device_cus()};
+    if (injected_failure()) return QLA_ERR_LAUNCH;
+    clear_stale_error();
     return qla::launch_correct_h0_grouped(a, table) == hipSuccess ? QLA_OK : QLA_ERR_LAUNCH;
 }
 
@@ -186,6 +219,8 @@ int qla_correct_h0_varlen(const float* H, const float* M, const float* S0, float
     if ((rc = check_buffers(H, M, S0, out, chains, segments, K, V)) != QLA_OK) return rc;
 
     qla::LaunchArgs a{H, M, S0, out, layout, direction, chains, heads, -1, K, V, stream, device_cus()};
+    if (injected_failure()) return QLA_ERR_LAUNCH;
+    clear_stale_error();
     return qla::launch_correct_h0_varlen(a, seqs) == hipSuccess ? QLA_OK : QLA_ERR_LAUNCH;
 }
 
