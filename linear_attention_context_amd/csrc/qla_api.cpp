@@ -138,6 +138,12 @@ QLA_API int qla_test_fail_launches(int n)
     g_fail_launches.store(n > 0 ? n : 0);
     return QLA_OK;
 }
+// 1 if a plain call of this shape runs two tiles per workgroup on a device
+// with `cus` compute units, else 0.
+QLA_API int qla_test_pairs_tiles(int K, long long chains, int V, int cus)
+{
+    return qla::plain_call_pairs_tiles(K, chains, V, cus) ? 1 : 0;
+}
 #endif
 
 int qla_correct_h0(const float* H, const float* M, const float* S0, float* out, int layout, int direction,

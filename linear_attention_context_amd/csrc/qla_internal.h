@@ -48,5 +48,8 @@ int max_threads_per_group();
 hipError_t launch_correct_h0(const LaunchArgs& a);
 hipError_t launch_correct_h0_grouped(const LaunchArgs& a, const GroupTable& table);
 hipError_t launch_correct_h0_varlen(const LaunchArgs& a, const SeqTable& seqs);
+// Whether a plain call of this shape runs two tiles per workgroup on a
+// device with `cus` compute units.
+bool plain_call_pairs_tiles(int K, long long chains, int V, int cus);
 
 }  // namespace qla

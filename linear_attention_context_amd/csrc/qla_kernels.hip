@@ -1600,6 +1600,26 @@ hipError_t launch_grouped_dir(const LaunchArgs& a, int tiles, const GroupTable& 
     return hipGetLastError();
 }
 
+// Whether a plain call runs two tiles per workgroup.  At K >= 96 one
+// workgroup fits in a CU's LDS with either kernel, so a call runs in rounds
+// of `cus` workgroups, and a two-tile workgroup takes 1.7-2.0x as long as a
+// one-tile one (measured at 8 and 32 segments).  Pairs pay off when they save
+// enough rounds: 1.8 r2 < r1 (at 1-2 tiles per CU one round against two, at
+// 3-4 two against four; at 2-3 tiles per CU two rounds of pairs lose to three
+// of single tiles).  Below K = 96 several workgroups share a CU, and pairs are
+// used from two tiles per CU on.
+template <int K>
+bool use_pairs(long long chains, int tiles, int cus)
+{
+    const long long t1 = chains * tiles, t2 = chains * ((tiles + 1) / 2);
+    if constexpr (K >= 96) {
+        const long long r1 = (t1 + cus - 1) / cus, r2 = (t2 + cus - 1) / cus;
+        return 9 * r2 < 5 * r1;
+    } else {
+        return t1 >= 2LL * cus;
+    }
+}
+
 // kind: 0 plain, 1 variable-length, 2 grouped.
 template <int K, int LAYOUT, int DIR>
 hipError_t launch_k(const LaunchArgs& a, int kind, const SeqTable* seqs, const GroupTable* table)
@@ -1613,10 +1633,9 @@ hipError_t launch_k(const LaunchArgs& a, int kind, const SeqTable* seqs, const G
             return hipGetLastError();
         }
         if constexpr (K % 32 == 0) {
-            // At least two 16-column tiles per CU: pairs of tiles, half a step
-            // apart, so that one tile's step boundary overlaps the other's
-            // matrix work.
-            if (kind == 0 && tiles >= 2 && (long long)a.chains * tiles >= 2LL * a.cus) {
+            // Pairs of tiles, half a step apart, so that one tile's step
+            // boundary overlaps the other's matrix work.
+            if (kind == 0 && tiles >= 2 && use_pairs<K>(a.chains, tiles, a.cus)) {
                 const int pairs = (tiles + 1) / 2;
                 hipLaunchKernelGGL((correct_h0_pair_kernel<K, LAYOUT, DIR>), dim3((unsigned)(a.chains * pairs)),
                                    dim3(dma_threads<K>()), 0, (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg,
@@ -1678,6 +1697,19 @@ hipError_t dispatch(const LaunchArgs& a, int layout, int direction, int kind, co
 }  // namespace
 
 int tiles_for(int V) { return (V + kTileV - 1) / kTileV; }
+
+bool plain_call_pairs_tiles(int K, long long chains, int V, int cus)
+{
+    const int tiles = tiles_for(V);
+    if (tiles < 2) return false;
+    switch (K) {
+    case 32: return use_pairs<32>(chains, tiles, cus);
+    case 64: return use_pairs<64>(chains, tiles, cus);
+    case 96: return use_pairs<96>(chains, tiles, cus);
+    case 128: return use_pairs<128>(chains, tiles, cus);
+    default: return false;
+    }
+}
 
 int max_threads_per_group() { return dma_threads<128>() > 64 * general_waves(true) ? dma_threads<128>() : 64 * general_waves(true); }
 

@@ -1,14 +1,17 @@
 """GPU tests of the two-tile producer kernel.
 
-Plain calls at K a multiple of 32 (up to 128) whose grid has at least two
-16-column tiles per compute unit run two tiles of a chain per workgroup, in
-two groups of MFMA waves half a step apart.  These shapes are sized past that
-threshold.  Every variant is compared with the fp64 oracle: with and without
+Plain calls at K a multiple of 32 (up to 128) run two tiles of a chain per
+workgroup, in two groups of MFMA waves half a step apart, where that saves
+rounds of workgroups (tests/test_pair_dispatch.py has the rule).  These shapes
+are sized into that range, and each test first checks that the launcher
+chooses the two-tile kernel for it.  Every variant is compared with the fp64 oracle: with and without
 S0, and with a ragged V whose last pair has one tile only.  Exact inputs and
 coded sentinels must come back bit for bit, chains of 1-3 segments exercise
 the barrier schedule's ends, and the forced-delay build and repeated calls
 must give identical bits.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -26,19 +29,26 @@ def _cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
-def _pair_shape(V):
-    """(batch, heads) with at least two 16-column tiles per compute unit."""
+def _pair_shape(K, V):
+    """(batch, heads) for which a plain call runs the two-tile kernel: at
+    K >= 96 more than three and at most four tiles per compute unit (two
+    rounds of pair workgroups), below at least two tiles per compute unit."""
+    import linear_attention_context_amd as qla
+    cus = _cus()
     tiles = (V + 15) // 16
-    chains = -(-2 * _cus() // tiles)
-    heads = -(-chains // 2)
-    return 2, heads
+    pairs = (tiles + 1) // 2
+    chains = 2 * cus // pairs if K >= 96 else -(-2 * cus // tiles)
+    lib = qla.load_library(qla.library_path("delay"))
+    lib.qla_test_pairs_tiles.argtypes = [ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_int]
+    assert lib.qla_test_pairs_tiles(K, chains, V, cus) == 1, (K, chains, V, cus)
+    return 1, chains
 
 
 @pytest.mark.parametrize("K", [32, 64, 96, 128])
 @pytest.mark.parametrize("layout,direction", VARIANTS)
 def test_pair_parity(K, layout, direction):
     V = 100 if K >= 64 else 52  # ragged: 7 or 4 tiles (the last pair of 7 has one tile)
-    B, NH = _pair_shape(V)
+    B, NH = _pair_shape(K, V)
     for with_s0 in (True, False):
         H, M, S0 = qi.random_case(3000 + K, (B, NH), 5, K, V, with_s0=with_s0)
         print(f"  pair K={K} V={V} {B}x{NH} {layout} {direction} s0={with_s0}", flush=True)
@@ -53,7 +63,7 @@ def test_pair_exact_inputs_and_sentinels(K, layout, direction):
     """Signed permutations with small integers (every fp32 operation exact)
     and the M = 0 coded sentinel: bit for bit."""
     V, n = 128, 4
-    B, NH = _pair_shape(V)
+    B, NH = _pair_shape(K, V)
     H = qi.small_integers(3100 + K, (B, NH, n, K, V))
     S0 = qi.small_integers(3102 + K, (B, NH, K, V))
     M = qi.signed_permutations(3101 + K, (B, NH, n), K)
@@ -71,7 +81,7 @@ def test_pair_exact_inputs_and_sentinels(K, layout, direction):
 @pytest.mark.parametrize("layout,direction", VARIANTS)
 def test_pair_short_chains(n, layout, direction):
     K = V = 128
-    B, NH = _pair_shape(V)
+    B, NH = _pair_shape(K, V)
     H, M, S0 = qi.random_case(3200 + n, (B, NH), n, K, V)
     got = run_hip(lay(H, layout), M, lay(S0, layout), layout, direction).cpu().numpy()
     ref = oracle_threaded(lay(H, layout), M, lay(S0, layout), layout, direction)
@@ -87,7 +97,7 @@ def test_pair_forced_delay_and_repeat_identical(layout, direction):
     import linear_attention_context_amd as qla
     delay = qla.load_library(qla.library_path("delay"))
     K, V, n = 128, 96, 6
-    B, NH = _pair_shape(V)
+    B, NH = _pair_shape(K, V)
     H, M, S0 = qi.random_case(3300, (B, NH), n, K, V)
     a = run_hip(lay(H, layout), M, lay(S0, layout), layout, direction)
     b = run_hip(lay(H, layout), M, lay(S0, layout), layout, direction, lib=delay)
