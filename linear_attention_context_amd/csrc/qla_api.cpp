@@ -138,11 +138,11 @@ QLA_API int qla_test_fail_launches(int n)
     g_fail_launches.store(n > 0 ? n : 0);
     return QLA_OK;
 }
-// 1 if a plain call of this shape runs two tiles per workgroup on a device
-// with `cus` compute units, else 0.
-QLA_API int qla_test_pairs_tiles(int K, long long chains, int V, int cus)
+// 1 if a plain call of this shape (chains of n_seg segments) runs two tiles
+// per workgroup on a device with `cus` compute units, else 0.
+QLA_API int qla_test_pairs_tiles(int K, long long chains, int V, int n_seg, int cus)
 {
-    return qla::plain_call_pairs_tiles(K, chains, V, cus) ? 1 : 0;
+    return qla::plain_call_pairs_tiles(K, chains, V, n_seg, cus) ? 1 : 0;
 }
 #endif
 

@@ -50,6 +50,6 @@ hipError_t launch_correct_h0_grouped(const LaunchArgs& a, const GroupTable& tabl
 hipError_t launch_correct_h0_varlen(const LaunchArgs& a, const SeqTable& seqs);
 // Whether a plain call of this shape runs two tiles per workgroup on a
 // device with `cus` compute units.
-bool plain_call_pairs_tiles(int K, long long chains, int V, int cus);
+bool plain_call_pairs_tiles(int K, long long chains, int V, int n_seg, int cus);
 
 }  // namespace qla

@@ -1600,23 +1600,25 @@ hipError_t launch_grouped_dir(const LaunchArgs& a, int tiles, const GroupTable& 
     return hipGetLastError();
 }
 
-// Whether a plain call runs two tiles per workgroup.  At K >= 96 one
-// workgroup fits in a CU's LDS with either kernel, so a call runs in rounds
-// of `cus` workgroups, and a two-tile workgroup takes 1.7-2.0x as long as a
-// one-tile one (measured at 8 and 32 segments).  Pairs pay off when they save
-// enough rounds: 1.8 r2 < r1 (at 1-2 tiles per CU one round against two, at
-// 3-4 two against four; at 2-3 tiles per CU two rounds of pairs lose to three
-// of single tiles).  Below K = 96 several workgroups share a CU, and pairs are
-// used from two tiles per CU on.
+// Whether a plain call runs two tiles per workgroup (measured on 256 CUs, 8
+// to 64 segments).  At K >= 96 one workgroup fits in a CU's LDS with either
+// kernel, so a call runs in rounds of `cus` workgroups, and a two-tile
+// workgroup takes 1.7-2.0x as long as a one-tile one: pairs pay off when they
+// save enough rounds, 1.8 r2 < r1 (at 1-2 tiles per CU one round against two,
+// at 3-4 two against four; at 2-3 tiles per CU two rounds of pairs lose to
+// three of single tiles).  Below K = 96 several workgroups share a CU: single
+// tiles win up to three tiles per CU, pairs above, and at K = 64 chains of 32
+// or more segments gain from pairs at 1-2 tiles per CU as well.
 template <int K>
-bool use_pairs(long long chains, int tiles, int cus)
+bool use_pairs(long long chains, int tiles, int n_seg, int cus)
 {
     const long long t1 = chains * tiles, t2 = chains * ((tiles + 1) / 2);
     if constexpr (K >= 96) {
         const long long r1 = (t1 + cus - 1) / cus, r2 = (t2 + cus - 1) / cus;
         return 9 * r2 < 5 * r1;
     } else {
-        return t1 >= 2LL * cus;
+        if (t1 > 3LL * cus) return true;
+        return K == 64 && n_seg >= 32 && t1 > cus && t1 <= 2LL * cus;
     }
 }
 
@@ -1635,7 +1637,7 @@ hipError_t launch_k(const LaunchArgs& a, int kind, const SeqTable* seqs, const G
         if constexpr (K % 32 == 0) {
             // Pairs of tiles, half a step apart, so that one tile's step
             // boundary overlaps the other's matrix work.
-            if (kind == 0 && tiles >= 2 && use_pairs<K>(a.chains, tiles, a.cus)) {
+            if (kind == 0 && tiles >= 2 && use_pairs<K>(a.chains, tiles, a.n_seg, a.cus)) {
                 const int pairs = (tiles + 1) / 2;
                 hipLaunchKernelGGL((correct_h0_pair_kernel<K, LAYOUT, DIR>), dim3((unsigned)(a.chains * pairs)),
                                    dim3(dma_threads<K>()), 0, (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg,
@@ -1698,15 +1700,15 @@ hipError_t dispatch(const LaunchArgs& a, int layout, int direction, int kind, co
 
 int tiles_for(int V) { return (V + kTileV - 1) / kTileV; }
 
-bool plain_call_pairs_tiles(int K, long long chains, int V, int cus)
+bool plain_call_pairs_tiles(int K, long long chains, int V, int n_seg, int cus)
 {
     const int tiles = tiles_for(V);
     if (tiles < 2) return false;
     switch (K) {
-    case 32: return use_pairs<32>(chains, tiles, cus);
-    case 64: return use_pairs<64>(chains, tiles, cus);
-    case 96: return use_pairs<96>(chains, tiles, cus);
-    case 128: return use_pairs<128>(chains, tiles, cus);
+    case 32: return use_pairs<32>(chains, tiles, n_seg, cus);
+    case 64: return use_pairs<64>(chains, tiles, n_seg, cus);
+    case 96: return use_pairs<96>(chains, tiles, n_seg, cus);
+    case 128: return use_pairs<128>(chains, tiles, n_seg, cus);
     default: return false;
     }
 }

@@ -29,18 +29,18 @@ def _cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
-def _pair_shape(K, V):
-    """(batch, heads) for which a plain call runs the two-tile kernel: at
-    K >= 96 more than three and at most four tiles per compute unit (two
-    rounds of pair workgroups), below at least two tiles per compute unit."""
+def _pair_shape(K, V, n):
+    """(batch, heads) for which a plain call runs the two-tile kernel: more
+    than three and at most four tiles per compute unit, at most two pair
+    workgroups per compute unit."""
     import linear_attention_context_amd as qla
     cus = _cus()
     tiles = (V + 15) // 16
     pairs = (tiles + 1) // 2
-    chains = 2 * cus // pairs if K >= 96 else -(-2 * cus // tiles)
+    chains = 2 * cus // pairs
     lib = qla.load_library(qla.library_path("delay"))
-    lib.qla_test_pairs_tiles.argtypes = [ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_int]
-    assert lib.qla_test_pairs_tiles(K, chains, V, cus) == 1, (K, chains, V, cus)
+    lib.qla_test_pairs_tiles.argtypes = [ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    assert lib.qla_test_pairs_tiles(K, chains, V, n, cus) == 1, (K, chains, V, n, cus)
     return 1, chains
 
 
@@ -48,7 +48,7 @@ def _pair_shape(K, V):
 @pytest.mark.parametrize("layout,direction", VARIANTS)
 def test_pair_parity(K, layout, direction):
     V = 100 if K >= 64 else 52  # ragged: 7 or 4 tiles (the last pair of 7 has one tile)
-    B, NH = _pair_shape(K, V)
+    B, NH = _pair_shape(K, V, 5)
     for with_s0 in (True, False):
         H, M, S0 = qi.random_case(3000 + K, (B, NH), 5, K, V, with_s0=with_s0)
         print(f"  pair K={K} V={V} {B}x{NH} {layout} {direction} s0={with_s0}", flush=True)
@@ -63,7 +63,7 @@ def test_pair_exact_inputs_and_sentinels(K, layout, direction):
     """Signed permutations with small integers (every fp32 operation exact)
     and the M = 0 coded sentinel: bit for bit."""
     V, n = 128, 4
-    B, NH = _pair_shape(K, V)
+    B, NH = _pair_shape(K, V, n)
     H = qi.small_integers(3100 + K, (B, NH, n, K, V))
     S0 = qi.small_integers(3102 + K, (B, NH, K, V))
     M = qi.signed_permutations(3101 + K, (B, NH, n), K)
@@ -81,7 +81,7 @@ def test_pair_exact_inputs_and_sentinels(K, layout, direction):
 @pytest.mark.parametrize("layout,direction", VARIANTS)
 def test_pair_short_chains(n, layout, direction):
     K = V = 128
-    B, NH = _pair_shape(K, V)
+    B, NH = _pair_shape(K, V, n)
     H, M, S0 = qi.random_case(3200 + n, (B, NH), n, K, V)
     got = run_hip(lay(H, layout), M, lay(S0, layout), layout, direction).cpu().numpy()
     ref = oracle_threaded(lay(H, layout), M, lay(S0, layout), layout, direction)
@@ -97,7 +97,7 @@ def test_pair_forced_delay_and_repeat_identical(layout, direction):
     import linear_attention_context_amd as qla
     delay = qla.load_library(qla.library_path("delay"))
     K, V, n = 128, 96, 6
-    B, NH = _pair_shape(K, V)
+    B, NH = _pair_shape(K, V, n)
     H, M, S0 = qi.random_case(3300, (B, NH), n, K, V)
     a = run_hip(lay(H, layout), M, lay(S0, layout), layout, direction)
     b = run_hip(lay(H, layout), M, lay(S0, layout), layout, direction, lib=delay)

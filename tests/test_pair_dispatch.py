@@ -4,9 +4,10 @@ library exports the launcher's decision as qla_test_pairs_tiles).
 At K >= 96 one workgroup of either kernel fills a CU's LDS, a call runs in
 rounds of one workgroup per CU, and a two-tile workgroup takes 1.7-2.0x as
 long as a one-tile one: pairs are chosen when 1.8 x their rounds is below the
-single tiles' rounds.  Below K = 96 they are chosen from two tiles per CU on.
-The expected decisions are those the measured timings favour on 256 CUs
-(K = V = 128 and 96, 8 and 32 segments)."""
+single tiles' rounds.  Below K = 96 several workgroups share a CU: pairs above
+three tiles per CU, and at K = 64 also at one to two tiles per CU for chains
+of 32 or more segments.  The expected decisions are those the measured
+timings favour on 256 CUs (K = 32 to 128, 8 to 64 segments)."""
 import ctypes
 import os
 
@@ -22,9 +23,9 @@ def rule():
         build.build()
     lib = qla.load_library(qla.library_path("delay"))
     f = lib.qla_test_pairs_tiles
-    f.argtypes = [ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_int]
+    f.argtypes = [ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     f.restype = ctypes.c_int
-    return lambda K, chains, V, cus=256: bool(f(K, chains, V, cus))
+    return lambda K, chains, V, n=8, cus=256: bool(f(K, chains, V, n, cus))
 
 
 @pytest.mark.parametrize("heads,pairs", [
@@ -33,8 +34,9 @@ def rule():
     (72, False), (80, False), (96, False),     # 2-3 per CU: two rounds of pairs lose to three
     (112, True), (128, True),                  # 3-4 per CU: two against four (the long chain, 4 x 32 heads)
 ])
-def test_k128_rounds(rule, heads, pairs):
-    assert rule(128, heads, 128) is pairs
+@pytest.mark.parametrize("n", [8, 64])
+def test_k128_rounds(rule, heads, pairs, n):
+    assert rule(128, heads, 128, n) is pairs
 
 
 @pytest.mark.parametrize("chains,pairs", [(42, False), (43, True), (64, True), (86, False), (128, False),
@@ -44,9 +46,21 @@ def test_k96_rounds(rule, chains, pairs):
     assert rule(96, chains, 96) is pairs
 
 
-def test_below_96_from_two_tiles_per_cu(rule):
-    assert not rule(64, 127, 64) and rule(64, 128, 64)   # 508 / 512 tiles
-    assert not rule(32, 255, 32) and rule(32, 256, 32)
+@pytest.mark.parametrize("chains,n,pairs", [
+    (96, 8, False), (128, 8, False), (160, 8, False), (192, 8, False),   # up to 3 tiles per CU
+    (193, 8, True), (256, 8, True), (384, 8, True),                      # above 3
+    (64, 32, False), (96, 32, True), (128, 32, True), (129, 32, False),  # long chains: 1-2 per CU too
+    (160, 64, False), (256, 64, True),
+])
+def test_k64(rule, chains, n, pairs):
+    # V = 64: four tiles per chain
+    assert rule(64, chains, 64, n) is pairs
+
+
+@pytest.mark.parametrize("chains,n,pairs", [(192, 64, False), (384, 64, False), (385, 64, True), (512, 8, True)])
+def test_k32(rule, chains, n, pairs):
+    # V = 32: two tiles per chain; no exception for long chains below three tiles per CU
+    assert rule(32, chains, 32, n) is pairs
 
 
 def test_never_for_single_tiles_or_other_k(rule):
@@ -65,3 +79,4 @@ def test_ragged_v_counts_pairs_per_chain(rule):
 def test_device_size_enters(rule):
     assert rule(128, 64, 128, cus=256)
     assert not rule(128, 64, 128, cus=512)
+    assert rule(64, 256, 64, cus=256) and not rule(64, 256, 64, cus=512)
