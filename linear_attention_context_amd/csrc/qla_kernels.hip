@@ -1388,7 +1388,7 @@ __global__ __launch_bounds__(dma_threads<K>()) void correct_h0_fwd_dma_kernel(
 }
 
 // Two 16-column tiles of a chain per workgroup (tiles tp and tp + pairs), half
-// a step apart (K a multiple of 32): grids of at least two tiles per CU.
+// a step apart (K a multiple of 32): plain calls for which use_pairs holds.
 template <int K, int LAYOUT, int DIR>
 __global__ __launch_bounds__(dma_threads<K>()) void correct_h0_pair_kernel(
     const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int pairs)
