@@ -1607,8 +1607,10 @@ hipError_t launch_grouped_dir(const LaunchArgs& a, int tiles, const GroupTable& 
 // save enough rounds, 1.8 r2 < r1 (at 1-2 tiles per CU one round against two,
 // at 3-4 two against four; at 2-3 tiles per CU two rounds of pairs lose to
 // three of single tiles).  Below K = 96 several workgroups share a CU: single
-// tiles win up to three tiles per CU, pairs above, and at K = 64 chains of 32
-// or more segments gain from pairs at 1-2 tiles per CU as well.
+// tiles win up to three tiles per CU and pairs at three to four; beyond four
+// the two are within 10% either way, and pairs are kept at K = 32, where they
+// win more often.  At K = 64 chains of 32 or more segments gain from pairs at
+// 1-2 tiles per CU as well.
 template <int K>
 bool use_pairs(long long chains, int tiles, int n_seg, int cus)
 {
@@ -1617,8 +1619,8 @@ bool use_pairs(long long chains, int tiles, int n_seg, int cus)
         const long long r1 = (t1 + cus - 1) / cus, r2 = (t2 + cus - 1) / cus;
         return 9 * r2 < 5 * r1;
     } else {
-        if (t1 > 3LL * cus) return true;
-        return K == 64 && n_seg >= 32 && t1 > cus && t1 <= 2LL * cus;
+        if (K == 64 && n_seg >= 32 && t1 > cus && t1 <= 2LL * cus) return true;
+        return t1 > 3LL * cus && (K != 64 || t1 <= 4LL * cus);
     }
 }
 

@@ -5,8 +5,8 @@ At K >= 96 one workgroup of either kernel fills a CU's LDS, a call runs in
 rounds of one workgroup per CU, and a two-tile workgroup takes 1.7-2.0x as
 long as a one-tile one: pairs are chosen when 1.8 x their rounds is below the
 single tiles' rounds.  Below K = 96 several workgroups share a CU: pairs above
-three tiles per CU, and at K = 64 also at one to two tiles per CU for chains
-of 32 or more segments.  The expected decisions are those the measured
+three tiles per CU (at K = 64 up to four), and at K = 64 also at one to two
+tiles per CU for chains of 32 or more segments.  The expected decisions are those the measured
 timings favour on 256 CUs (K = 32 to 128, 8 to 64 segments)."""
 import ctypes
 import os
@@ -48,7 +48,7 @@ def test_k96_rounds(rule, chains, pairs):
 
 @pytest.mark.parametrize("chains,n,pairs", [
     (96, 8, False), (128, 8, False), (160, 8, False), (192, 8, False),   # up to 3 tiles per CU
-    (193, 8, True), (256, 8, True), (384, 8, True),                      # above 3
+    (193, 8, True), (256, 8, True), (257, 8, False), (384, 8, False),    # 3-4 only
     (64, 32, False), (96, 32, True), (128, 32, True), (129, 32, False),  # long chains: 1-2 per CU too
     (160, 64, False), (256, 64, True),
 ])
