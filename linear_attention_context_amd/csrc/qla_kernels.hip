@@ -1491,6 +1491,15 @@ constexpr int grouped_threads()
     return 64 * Grouped<K>::WAVES;
 }
 
+// The variant (2 * layout + direction) of the head group holding `head`.
+__device__ __forceinline__ int group_variant(int head, const GroupTable& table)
+{
+    int variant = 0;
+    for (int i = 0; i < table.n; ++i)
+        if (head >= table.begin[i] && head < table.begin[i] + table.count[i]) variant = table.variant[i];
+    return variant;
+}
+
 template <int K>
 __global__ __launch_bounds__((grouped_threads<K>())) void correct_h0_grouped_kernel(
     const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int tiles, int heads,
@@ -1500,15 +1509,34 @@ __global__ __launch_bounds__((grouped_threads<K>())) void correct_h0_grouped_ker
     const int id = xcd_logical_id(blockIdx.x, gridDim.x);
     const int chain = id / tiles;
     const int tile = id - chain * tiles;
-    const int head = chain % heads;
-    int variant = 0;
-    for (int i = 0; i < table.n; ++i)
-        if (head >= table.begin[i] && head < table.begin[i] + table.count[i]) variant = table.variant[i];
-    switch (variant) {
+    switch (group_variant(chain % heads, table)) {
     case 0: DmaChain<K, QLA_LAYOUT_KV, QLA_DIR_FWD>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
     case 1: DmaChain<K, QLA_LAYOUT_KV, QLA_DIR_BWD>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
     case 2: DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_FWD>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
     default: DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_BWD>::run(H, M, S0, out, n_seg, V, (size_t)chain, tile, lds); break;
+    }
+}
+
+// The grouped call with two tiles of a chain per workgroup (K a multiple of
+// 32), chosen by the same rule as for plain calls: each head group's chains
+// run the plain calls' two-tile code for its variant.
+template <int K>
+__global__ __launch_bounds__((grouped_threads<K>())) void correct_h0_grouped_pair_kernel(
+    const float* H, const float* __restrict__ M, const float* S0, float* out, int n_seg, int V, int pairs, int heads,
+    GroupTable table)
+{
+    static_assert(DmaChain<K, QLA_LAYOUT_KV, QLA_DIR_FWD, 2>::LDS_FLOATS <= Grouped<K>::LDS_FLOATS &&
+                      DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_BWD, 2>::LDS_FLOATS <= Grouped<K>::LDS_FLOATS,
+                  "the two-tile chains fit the grouped LDS");
+    __shared__ __attribute__((aligned(16))) float lds[Grouped<K>::LDS_FLOATS];
+    const int id = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int chain = id / pairs;
+    const int tp = id - chain * pairs;
+    switch (group_variant(chain % heads, table)) {
+    case 0: DmaChain<K, QLA_LAYOUT_KV, QLA_DIR_FWD, 2>::run(H, M, S0, out, n_seg, V, (size_t)chain, tp, lds); break;
+    case 1: DmaChain<K, QLA_LAYOUT_KV, QLA_DIR_BWD, 2>::run(H, M, S0, out, n_seg, V, (size_t)chain, tp, lds); break;
+    case 2: DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_FWD, 2>::run(H, M, S0, out, n_seg, V, (size_t)chain, tp, lds); break;
+    default: DmaChain<K, QLA_LAYOUT_VK, QLA_DIR_BWD, 2>::run(H, M, S0, out, n_seg, V, (size_t)chain, tp, lds); break;
     }
 }
 
@@ -1632,6 +1660,15 @@ hipError_t launch_k(const LaunchArgs& a, int kind, const SeqTable* seqs, const G
     const dim3 grid((unsigned)(a.chains * tiles));
     if constexpr (K <= 128) {
         if (kind == 2) {
+            if constexpr (K % 32 == 0) {
+                if (tiles >= 2 && use_pairs<K>(a.chains, tiles, a.n_seg, a.cus)) {
+                    const int pairs = (tiles + 1) / 2;
+                    hipLaunchKernelGGL((correct_h0_grouped_pair_kernel<K>), dim3((unsigned)(a.chains * pairs)),
+                                       dim3(grouped_threads<K>()), 0, (hipStream_t)a.stream, a.H, a.M, a.S0, a.out,
+                                       a.n_seg, a.V, pairs, a.heads, *table);
+                    return hipGetLastError();
+                }
+            }
             hipLaunchKernelGGL((correct_h0_grouped_kernel<K>), grid, dim3(grouped_threads<K>()), 0,
                                (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, tiles, a.heads, *table);
             return hipGetLastError();

@@ -109,3 +109,43 @@ def test_pair_forced_delay_and_repeat_identical(layout, direction):
         qla.qla_correct_h0(Hd, Md, Sd, out, layout, direction, B, NH, n, K, V)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int32).cpu(), a.view(torch.int32).cpu())
+
+
+@pytest.mark.parametrize("K", [64, 128])
+def test_pair_grouped(K):
+    """A grouped call in the two-tile range (the same rule as plain calls):
+    every head group against the fp64 oracle, and a call with one group equal,
+    bit for bit, to the plain call of that variant."""
+    import torch
+
+    import linear_attention_context_amd as qla
+    V, n = 128, 4
+    B, NH = _pair_shape(K, V, n)
+    q = NH // 4
+    groups = [(0, q, "kv", "fwd"), (q, q, "vk", "bwd"), (2 * q, q, "vk", "fwd"), (3 * q, NH - 3 * q, "kv", "bwd")]
+    H, M, S0 = qi.random_case(3400 + K, (B, NH), n, K, V)
+    # vk heads store V x K matrices; every head is K*V floats per state either way
+    Hs, Ss = H.copy(), S0.copy()
+    for begin, count, layout, _ in groups:
+        if layout == "vk":
+            Hs[:, begin:begin + count] = qi.to_vk(H[:, begin:begin + count]).reshape(H[:, begin:begin + count].shape)
+            Ss[:, begin:begin + count] = qi.to_vk(S0[:, begin:begin + count]).reshape(S0[:, begin:begin + count].shape)
+    Hd, Md, Sd = to_device(Hs), to_device(M), to_device(Ss)
+    out = torch.full_like(Hd, float("nan"))
+    print(f"  grouped pair K={K} {B}x{NH}", flush=True)
+    qla.qla_correct_h0_grouped(Hd, Md, Sd, out, groups, B, NH, n, K, V)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for begin, count, layout, direction in groups:
+        sl = slice(begin, begin + count)
+        shape = (B, count, n, K, V) if layout == "kv" else (B, count, n, V, K)
+        Hh = Hs[:, sl].reshape(shape)
+        Sh = Ss[:, sl].reshape(shape[:2] + shape[3:])
+        ref = oracle_threaded(Hh, M[:, sl], Sh, layout, direction)
+        assert_parity(got[:, sl].reshape(shape), ref, f"grouped pair K={K} {layout} {direction}")
+    # one group: the plain call's kernel and bits
+    one = torch.full_like(Hd, float("nan"))
+    qla.qla_correct_h0_grouped(to_device(H), Md, to_device(S0), one, [(0, NH, "kv", "fwd")], B, NH, n, K, V)
+    plain = run_hip(H, M, S0, "kv", "fwd")
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int32).cpu(), plain.view(torch.int32).cpu())
