@@ -1457,6 +1457,21 @@ __global__ __launch_bounds__(dma_threads<K>()) void correct_h0_fwd_dma_varlen_ke
     D::run_chain(C, S0 ? S0 + (size_t)chain * K * V : nullptr, V, tile, lds);
 }
 
+// Variable-length chains with two tiles per workgroup (K a multiple of 32).
+template <int K, int LAYOUT, int DIR>
+__global__ __launch_bounds__(dma_threads<K>()) void correct_h0_pair_varlen_kernel(
+    const float* H, const float* __restrict__ M, const float* S0, float* out, int heads, int V, int pairs,
+    SeqTable seqs)
+{
+    using D = DmaChain<K, LAYOUT, DIR, 2>;
+    __shared__ __attribute__((aligned(16))) float lds[D::LDS_FLOATS];
+    const int id = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int chain = id / pairs;
+    const int tp = id - chain * pairs;
+    const auto C = varlen_chain<typename D::Chain>(H, M, out, heads, V, chain, seqs, K);
+    D::run_chain(C, S0 ? S0 + (size_t)chain * K * V : nullptr, V, tp, lds);
+}
+
 template <int K, int LAYOUT>
 __global__ __launch_bounds__(dma_threads<K>()) void correct_h0_bwd_dma_varlen_kernel(
     const float* H, const float* __restrict__ M, const float* S0, float* out, int heads, int V, int tiles,
@@ -1652,6 +1667,12 @@ bool use_pairs(long long chains, int tiles, int n_seg, int cus)
     }
 }
 
+// Mean segments per sequence of a variable-length call.
+inline int mean_segments(const SeqTable& seqs)
+{
+    return seqs.n > 0 ? (seqs.offs[seqs.n] - seqs.offs[0]) / seqs.n : 0;
+}
+
 // kind: 0 plain, 1 variable-length, 2 grouped.
 template <int K, int LAYOUT, int DIR>
 hipError_t launch_k(const LaunchArgs& a, int kind, const SeqTable* seqs, const GroupTable* table)
@@ -1675,12 +1696,18 @@ hipError_t launch_k(const LaunchArgs& a, int kind, const SeqTable* seqs, const G
         }
         if constexpr (K % 32 == 0) {
             // Pairs of tiles, half a step apart, so that one tile's step
-            // boundary overlaps the other's matrix work.
-            if (kind == 0 && tiles >= 2 && use_pairs<K>(a.chains, tiles, a.n_seg, a.cus)) {
+            // boundary overlaps the other's matrix work (variable-length
+            // calls: judged by their mean chain length).
+            const int n = kind == 1 ? mean_segments(*seqs) : a.n_seg;
+            if (tiles >= 2 && use_pairs<K>(a.chains, tiles, n, a.cus)) {
                 const int pairs = (tiles + 1) / 2;
-                hipLaunchKernelGGL((correct_h0_pair_kernel<K, LAYOUT, DIR>), dim3((unsigned)(a.chains * pairs)),
-                                   dim3(dma_threads<K>()), 0, (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg,
-                                   a.V, pairs);
+                const dim3 pgrid((unsigned)(a.chains * pairs));
+                if (kind == 1)
+                    hipLaunchKernelGGL((correct_h0_pair_varlen_kernel<K, LAYOUT, DIR>), pgrid, dim3(dma_threads<K>()),
+                                       0, (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.heads, a.V, pairs, *seqs);
+                else
+                    hipLaunchKernelGGL((correct_h0_pair_kernel<K, LAYOUT, DIR>), pgrid, dim3(dma_threads<K>()), 0,
+                                       (hipStream_t)a.stream, a.H, a.M, a.S0, a.out, a.n_seg, a.V, pairs);
                 return hipGetLastError();
             }
         }

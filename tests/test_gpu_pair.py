@@ -149,3 +149,43 @@ def test_pair_grouped(K):
     plain = run_hip(H, M, S0, "kv", "fwd")
     torch.cuda.synchronize()
     assert torch.equal(one.view(torch.int32).cpu(), plain.view(torch.int32).cpu())
+
+
+def _pairs_rule(K, chains, V, n):
+    import linear_attention_context_amd as qla
+    lib = qla.load_library(qla.library_path("delay"))
+    lib.qla_test_pairs_tiles.argtypes = [ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    return lib.qla_test_pairs_tiles(K, chains, V, n, _cus()) == 1
+
+
+@pytest.mark.parametrize("layout,direction", VARIANTS)
+def test_pair_varlen(layout, direction):
+    """Variable-length chains in the two-tile range (judged by the mean chain
+    length): ragged lengths with an empty sequence against the fp64 oracle, and
+    equal lengths bit for bit against the fixed-length call."""
+    import torch
+
+    import linear_attention_context_amd as qla
+    K = V = 128
+    heads = 2 * _cus() // 4 // 4  # 4 sequences of `heads` chains: 2 pair workgroups per CU
+    seg_counts = [3, 5, 0, 6]
+    assert _pairs_rule(K, 4 * heads, V, sum(seg_counts) // 4)
+    H, M, S0, offs = qi.varlen_case(3500, seg_counts, heads, K, V)
+    ref = oracle.correct_h0_varlen(lay(H, layout), M, lay(S0, layout), offs, heads, layout, direction)
+    Hd, Md, Sd = to_device(lay(H, layout)), to_device(M), to_device(lay(S0, layout))
+    out = torch.full_like(Hd, float("nan"))
+    print(f"  pair varlen {layout} {direction} heads={heads} segs={seg_counts}", flush=True)
+    qla.qla_correct_h0_varlen(Hd, Md, Sd, out, layout, direction, offs, heads, K, V)
+    torch.cuda.synchronize()
+    assert_parity(out.cpu().numpy(), ref, f"pair varlen {layout} {direction}")
+    # equal lengths: the fixed-length call's kernel and bits
+    n = 4
+    H, M, S0, offs = qi.varlen_case(3600, [n] * 4, heads, K, V)
+    Hl, Sl = lay(H, layout), lay(S0, layout)
+    Hd, Md, Sd = to_device(Hl), to_device(M), to_device(Sl)
+    var = torch.full_like(Hd, float("nan"))
+    qla.qla_correct_h0_varlen(Hd, Md, Sd, var, layout, direction, offs, heads, K, V)
+    fixed = run_hip(Hl.reshape((4, heads, n) + Hl.shape[1:]), M.reshape(4, heads, n, K, K),
+                    Sl.reshape((4, heads) + Sl.shape[2:]), layout, direction)
+    torch.cuda.synchronize()
+    assert torch.equal(var.view(torch.int32).cpu().flatten(), fixed.view(torch.int32).cpu().flatten())

@@ -33,10 +33,10 @@ VMEM = re.compile(r"^(buffer_|global_)")
 # kernels with producer waves: the plain and variable-length K <= 128 kernels of
 # both directions, and the grouped kernel at K <= 128 (mangled names)
 K_DMA = (16, 32, 48, 64, 80, 96, 112, 128)
-# and the two-tile kernels (plain and grouped) at K a multiple of 32
+# and the two-tile kernels (plain, variable-length and grouped) at K a multiple of 32
 K_PAIR = tuple(k for k in K_DMA if k % 32 == 0)
 PRODUCER_KERNELS = re.compile(r"correct_h0_(fwd|bwd)_dma|correct_h0_pair_kernel|correct_h0_grouped_kernelILi(%s)E"
-                              r"|correct_h0_grouped_pair_kernel" % "|".join(map(str, K_DMA)))
+                              r"|correct_h0_grouped_pair_kernel|correct_h0_pair_varlen_kernel" % "|".join(map(str, K_DMA)))
 
 
 def _tools():
@@ -110,8 +110,9 @@ def test_producer_barriers_cover_every_copy(name, tmp_path):
         pytest.skip(f"{name} is not built")
     kernels = list(_kernels(_disassemble(lib, tmp_path)))
     # {fwd, bwd} x {kv, vk} x {plain, variable-length} at each K <= 128, and the grouped kernel there;
-    # {fwd, bwd} x {kv, vk} two-tile kernels and the grouped two-tile kernel at each K that is a multiple of 32
-    assert len(kernels) == 9 * len(K_DMA) + 5 * len(K_PAIR), [k for k, _ in kernels]
+    # {fwd, bwd} x {kv, vk} x {plain, variable-length} two-tile kernels and the grouped two-tile kernel
+    # at each K that is a multiple of 32
+    assert len(kernels) == 9 * len(K_DMA) + 9 * len(K_PAIR), [k for k, _ in kernels]
     for sym, body in kernels:
         checked, problems = _check(body)
         # the barrier after the first copy and the one in the step loop, at least
