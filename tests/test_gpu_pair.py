@@ -114,8 +114,9 @@ def test_pair_forced_delay_and_repeat_identical(layout, direction):
 @pytest.mark.parametrize("K", [64, 128])
 def test_pair_grouped(K):
     """A grouped call in the two-tile range (the same rule as plain calls):
-    every head group against the fp64 oracle, and a call with one group equal,
-    bit for bit, to the plain call of that variant."""
+    every head group against the fp64 oracle, the forced-delay build giving the
+    same bits, and a call with one group equal, bit for bit, to the plain call
+    of that variant."""
     import torch
 
     import linear_attention_context_amd as qla
@@ -143,6 +144,11 @@ def test_pair_grouped(K):
         Sh = Ss[:, sl].reshape(shape[:2] + shape[3:])
         ref = oracle_threaded(Hh, M[:, sl], Sh, layout, direction)
         assert_parity(got[:, sl].reshape(shape), ref, f"grouped pair K={K} {layout} {direction}")
+    delayed = torch.full_like(Hd, float("nan"))
+    qla.qla_correct_h0_grouped(Hd, Md, Sd, delayed, groups, B, NH, n, K, V,
+                               lib=qla.load_library(qla.library_path("delay")))
+    torch.cuda.synchronize()
+    assert torch.equal(delayed.view(torch.int32), out.view(torch.int32))
     # one group: the plain call's kernel and bits
     one = torch.full_like(Hd, float("nan"))
     qla.qla_correct_h0_grouped(to_device(H), Md, to_device(S0), one, [(0, NH, "kv", "fwd")], B, NH, n, K, V)
@@ -161,8 +167,9 @@ def _pairs_rule(K, chains, V, n):
 @pytest.mark.parametrize("layout,direction", VARIANTS)
 def test_pair_varlen(layout, direction):
     """Variable-length chains in the two-tile range (judged by the mean chain
-    length): ragged lengths with an empty sequence against the fp64 oracle, and
-    equal lengths bit for bit against the fixed-length call."""
+    length): ragged lengths with an empty sequence against the fp64 oracle, the
+    forced-delay build giving the same bits, and equal lengths bit for bit
+    against the fixed-length call."""
     import torch
 
     import linear_attention_context_amd as qla
@@ -178,6 +185,11 @@ def test_pair_varlen(layout, direction):
     qla.qla_correct_h0_varlen(Hd, Md, Sd, out, layout, direction, offs, heads, K, V)
     torch.cuda.synchronize()
     assert_parity(out.cpu().numpy(), ref, f"pair varlen {layout} {direction}")
+    delayed = torch.full_like(Hd, float("nan"))
+    qla.qla_correct_h0_varlen(Hd, Md, Sd, delayed, layout, direction, offs, heads, K, V,
+                              lib=qla.load_library(qla.library_path("delay")))
+    torch.cuda.synchronize()
+    assert torch.equal(delayed.view(torch.int32), out.view(torch.int32))
     # equal lengths: the fixed-length call's kernel and bits
     n = 4
     H, M, S0, offs = qi.varlen_case(3600, [n] * 4, heads, K, V)
